@@ -1,0 +1,167 @@
+/*
+ * snapkv.h -- C ABI of libsnapkv: SnapKV prefill-time KV-cache compression on
+ * one AMD MI355X (gfx950).
+ *
+ * The method is the one described on the page
+ * "論文解説: SnapKV — アテンションパターン観測によるKVキャッシュ圧縮"
+ * (0h-n0.github.io/posts/paper-2404-14469/):
+ *   - プロンプトの分割: each request of L tokens is split into a prefix of
+ *     P = L - L_obs positions and an observation window of the last L_obs.
+ *   - 投票メカニズム: for every query head, the L_obs window queries attend
+ *     (softmax of q k^T / sqrt(d)) to the keys; the weights are summed over the
+ *     window rows into a vote C per prefix position.  Under grouped-query
+ *     attention the G = H_q / H_kv query heads that share a KV head add their
+ *     votes (query head h reads KV head h / G).
+ *   - クラスタリングによる文脈保持: C is max-pooled with width K_pool, stride 1,
+ *     padding K_pool/2 (windows are clipped at the prefix ends).
+ *   - top-k: k = floor(p * P) (ratio mode) or min(budget, P) (budget mode)
+ *     positions per (request, KV head), ties broken toward the lower position,
+ *     emitted in ascending order (アルゴリズム listing: top-k, then sort).
+ *   - the chosen K/V rows are gathered and the full window K/V is appended.
+ * Softmax denominator: by default every key a window row can see, i.e. the
+ * prefix plus the window up to and including the row's own position (causal
+ * inside the window).  SNAPKV_PREFIX_ONLY selects the listing's variant whose
+ * softmax runs over the prefix keys only.
+ *
+ * Conventions shared by every call:
+ *   - Device pointers unless a name ends in _host.  The caller owns every
+ *     buffer; the library never allocates and keeps no per-call state.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  Outputs are valid once the
+ *     stream reaches that point.  Calls on different streams must use
+ *     different workspaces.
+ *   - All argument checks run on the host before any launch: on an error the
+ *     call returns a negative snapkv_status, launches nothing and writes
+ *     nothing.  After launching, a HIP launch error returns SNAPKV_EHIP and
+ *     leaves the outputs undefined.
+ *   - Pointers must be 16-byte aligned and K/V strides must keep every row
+ *     16-byte aligned.  Inputs and outputs must not alias.  Inputs must be
+ *     finite (not checked: a check would cost a pass over K).
+ *
+ * Layouts (elements of the problem's dtype unless stated):
+ *   q_obs   [B][H_q][L_obs][d], contiguous: the last L_obs queries of every
+ *           request and query head.
+ *   K, V    token-packed: element (g, t, c) at g*kv_head_stride +
+ *           t*kv_token_stride + c, t in [0, T), T = cu_seqlens[B]; request r
+ *           owns tokens [cu_seqlens[r], cu_seqlens[r+1]).  Head-major
+ *           [H_kv][T][d] and token-major [T][H_kv][d] are both expressible.
+ *   votes,
+ *   pooled  float32 [H_kv][sum_r P_r]: (g, r, j) at g*sum_P + cu_pfx[r] + j.
+ *   idx     int32 [H_kv][sum_r k_r]: (g, r, t) at g*sum_k + cu_k[r] + t, the
+ *           request-local prefix positions in [0, P_r), strictly ascending.
+ *   K_out,
+ *   V_out   [H_kv][sum_r (k_r + L_obs)][d], contiguous: rows cu_out[r] ..
+ *           cu_out[r+1]-1 of head g hold request r's chosen rows (ascending
+ *           position) followed by its L_obs window rows in order.
+ */
+#ifndef SNAPKV_H
+#define SNAPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SNAPKV_OK = 0,
+    SNAPKV_EINVAL = -1,       /* an argument is invalid (message: snapkv_last_error) */
+    SNAPKV_EWORKSPACE = -2,   /* workspace missing, misaligned or smaller than snapkv_plan asks */
+    SNAPKV_EUNSUPPORTED = -3, /* valid but not supported: head_dim, G*L_obs > 256, device */
+    SNAPKV_EHIP = -4          /* the HIP runtime reported an error */
+} snapkv_status;
+
+typedef enum { SNAPKV_F32 = 0, SNAPKV_BF16 = 1 } snapkv_dtype;
+typedef enum { SNAPKV_RATIO = 0, SNAPKV_BUDGET = 1 } snapkv_mode;
+typedef enum { SNAPKV_CAUSAL_WINDOW = 0, SNAPKV_PREFIX_ONLY = 1 } snapkv_variant;
+
+/* flags */
+#define SNAPKV_FLAG_TWO_PASS 0x1u /* score with two passes over K (stats, then votes) */
+
+typedef struct {
+    int32_t batch;            /* B >= 1 requests */
+    int32_t num_q_heads;      /* H_q >= 1 */
+    int32_t num_kv_heads;     /* H_kv >= 1, H_q % H_kv == 0 */
+    int32_t head_dim;         /* d: 64 or 128 */
+    int32_t obs_window;       /* L_obs >= 1 */
+    int32_t pool_kernel;      /* K_pool, odd, >= 1 */
+    int32_t mode;             /* snapkv_mode */
+    int32_t dtype;            /* snapkv_dtype of q_obs, K, V, K_out, V_out */
+    int32_t variant;          /* snapkv_variant */
+    uint32_t flags;           /* SNAPKV_FLAG_* */
+    double ratio;             /* p in (0, 1], ratio mode */
+    int64_t budget;           /* >= 0, budget mode */
+    int64_t kv_head_stride;   /* elements between KV heads of K and V */
+    int64_t kv_token_stride;  /* elements between tokens of K and V */
+    const int32_t *cu_seqlens_host; /* host [B+1]: 0 = cu[0] <= ..., L_r = cu[r+1]-cu[r] >= L_obs */
+} snapkv_problem;
+
+/*
+ * snapkv_plan -- validate a problem and size its outputs and workspace.
+ * Host only; touches no device.  Every output pointer may be NULL.
+ *   k_host      [B]   : k_r = floor(p * P_r) or min(budget, P_r)
+ *                       (投票メカニズム: k = floor(p * L_prefix); listing: min(max_cap, pfx)).
+ *   cu_pfx_host [B+1] : exclusive prefix sums of P_r (votes/pooled offsets).
+ *   cu_k_host   [B+1] : exclusive prefix sums of k_r (idx offsets).
+ *   cu_out_host [B+1] : exclusive prefix sums of k_r + L_obs (K_out/V_out rows).
+ *   ws_bytes          : workspace bytes that snapkv_scores, snapkv_select and
+ *                       snapkv_compress need for this problem on the current
+ *                       device (0 is never returned).
+ * Returns SNAPKV_OK or SNAPKV_EINVAL / SNAPKV_EUNSUPPORTED.
+ */
+int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host, int64_t *cu_k_host,
+                int64_t *cu_out_host, size_t *ws_bytes);
+
+/*
+ * snapkv_scores -- votes and pooled votes (投票メカニズム; クラスタリングによる文脈保持).
+ *   q_obs, K : inputs as laid out above (dtype of the problem).
+ *   votes    : out, float32 [H_kv][sum_P], or NULL to skip writing C.
+ *   pooled   : out, float32 [H_kv][sum_P], max pooled votes.
+ *   ws       : device workspace of at least snapkv_plan's ws_bytes, 256-byte aligned.
+ */
+int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, float *votes, float *pooled,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * snapkv_select -- top-k of the pooled votes per (request, KV head): the k_r
+ * largest values, ties to the lower position, written ascending
+ * (投票メカニズム I = Top_k; アルゴリズム listing: topk then sort).
+ *   pooled : float32 [H_kv][sum_P], values >= 0 (as snapkv_scores writes them).
+ *   idx    : out, int32 [H_kv][sum_k].
+ */
+int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, void *ws, size_t ws_bytes,
+                  void *stream);
+
+/*
+ * snapkv_gather -- compressed cache rows (アルゴリズム listing: gather per head,
+ * then concat with the window).  Copies bytes; no arithmetic.
+ *   K, V         : inputs (strided as above).
+ *   idx          : int32 [H_kv][sum_k], ascending request-local positions < P_r.
+ *   K_out, V_out : out, [H_kv][sum_out][d] contiguous.
+ */
+int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const int32_t *idx, void *K_out,
+                  void *V_out, void *stream);
+
+/*
+ * snapkv_compress -- the whole path: scores, select, gather.
+ *   idx    : out, int32 [H_kv][sum_k], or NULL (then kept in the workspace).
+ *   pooled : out, float32 [H_kv][sum_P], or NULL (then kept in the workspace).
+ */
+int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
+                    void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream);
+
+/* Text of a status code; never NULL. */
+const char *snapkv_strerror(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *snapkv_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int snapkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SNAPKV_H */

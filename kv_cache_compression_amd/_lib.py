@@ -1,0 +1,259 @@
+"""ctypes binding of libsnapkv (the C ABI in include/snapkv.h).
+
+Argument marshalling only: every step of the compression runs in the library's
+HIP kernels.  Tensors are torch tensors on the current CUDA (HIP) device; work
+is enqueued on ``torch.cuda.current_stream()``.  There is no fallback: if the
+library is not built, or the device is not gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsnapkv.so")
+
+OK, EINVAL, EWORKSPACE, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+RATIO, BUDGET = 0, 1
+CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
+FLAG_TWO_PASS = 0x1
+
+SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
+           "snapkv_strerror", "snapkv_last_error", "snapkv_version")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of snapkv_problem."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("obs_window", ctypes.c_int32),
+        ("pool_kernel", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("ratio", ctypes.c_double),
+        ("budget", ctypes.c_int64),
+        ("kv_head_stride", ctypes.c_int64),
+        ("kv_token_stride", ctypes.c_int64),
+        ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+class SnapKVError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__("%s: %s (%s)" % (where, detail or "error", status))
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load() -> ctypes.CDLL:
+    """Load libsnapkv.so; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError("libsnapkv.so is not built: run `python -m kv_cache_compression_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, sz = ctypes.c_void_p, ctypes.c_size_t
+            P = ctypes.POINTER(Problem)
+            i64p = ctypes.POINTER(ctypes.c_int64)
+            lib.snapkv_plan.argtypes = [P, i64p, i64p, i64p, i64p, ctypes.POINTER(sz)]
+            lib.snapkv_scores.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
+            lib.snapkv_select.argtypes = [P, vp, vp, vp, sz, vp]
+            lib.snapkv_gather.argtypes = [P, vp, vp, vp, vp, vp, vp]
+            lib.snapkv_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress"):
+                getattr(lib, f).restype = ctypes.c_int
+            lib.snapkv_strerror.argtypes = [ctypes.c_int]
+            lib.snapkv_strerror.restype = ctypes.c_char_p
+            lib.snapkv_last_error.argtypes = []
+            lib.snapkv_last_error.restype = ctypes.c_char_p
+            lib.snapkv_version.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status == OK:
+        return
+    lib = load()
+    detail = lib.snapkv_last_error().decode() or lib.snapkv_strerror(status).decode()
+    if status in (EINVAL, EWORKSPACE, EUNSUPPORTED):
+        err = ValueError("%s: %s (status %d)" % (where, detail, status))
+        err.status = status
+        raise err
+    raise SnapKVError(status, where, detail)
+
+
+class Spec:
+    """A validated problem: the C struct plus host-side sizes from snapkv_plan."""
+
+    def __init__(self, *, batch, num_q_heads, num_kv_heads, head_dim, obs_window, pool_kernel, ratio, budget,
+                 dtype, cu_seqlens, kv_head_stride, kv_token_stride, variant=CAUSAL_WINDOW, two_pass=False):
+        if (ratio is None) == (budget is None):
+            raise ValueError("give exactly one of ratio and budget")
+        self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        if self.cu.shape != (batch + 1,):
+            raise ValueError("cu_seqlens must have batch + 1 entries")
+        pb = Problem()
+        pb.batch, pb.num_q_heads, pb.num_kv_heads, pb.head_dim = batch, num_q_heads, num_kv_heads, head_dim
+        pb.obs_window, pb.pool_kernel = obs_window, pool_kernel
+        pb.mode = RATIO if ratio is not None else BUDGET
+        pb.dtype = dtype
+        pb.variant = variant
+        pb.flags = FLAG_TWO_PASS if two_pass else 0
+        pb.ratio = float(ratio) if ratio is not None else 0.0
+        pb.budget = int(budget) if budget is not None else 0
+        pb.kv_head_stride, pb.kv_token_stride = int(kv_head_stride), int(kv_token_stride)
+        pb.cu_seqlens_host = self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        self.pb = pb
+        self.k = np.zeros(batch, np.int64)
+        self.cu_pfx = np.zeros(batch + 1, np.int64)
+        self.cu_k = np.zeros(batch + 1, np.int64)
+        self.cu_out = np.zeros(batch + 1, np.int64)
+        ws = ctypes.c_size_t(0)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        st = load().snapkv_plan(ctypes.byref(pb), self.k.ctypes.data_as(i64p), self.cu_pfx.ctypes.data_as(i64p),
+                                self.cu_k.ctypes.data_as(i64p), self.cu_out.ctypes.data_as(i64p), ctypes.byref(ws))
+        _check(st, "snapkv_plan")
+        self.ws_bytes = int(ws.value)
+        self.Hkv = num_kv_heads
+        self.sum_P = int(self.cu_pfx[-1])
+        self.sum_k = int(self.cu_k[-1])
+        self.sum_out = int(self.cu_out[-1])
+        self.head_dim = head_dim
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError("q_obs/K/V must be bfloat16 or float32")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant=CAUSAL_WINDOW,
+              two_pass=False) -> Spec:
+    """Validate shapes of q_obs [B, H_q, L_obs, d] and K [H_kv, T, d] (any strides, last dim contiguous)."""
+    if q_obs.dim() != 4 or K.dim() != 3:
+        raise ValueError("q_obs must be [B, H_q, L_obs, d] and K [H_kv, T, d]")
+    B, Hq, w, d = q_obs.shape
+    Hkv, T, dk = K.shape
+    if dk != d or w != obs_window:
+        raise ValueError("head_dim / obs_window mismatch between q_obs and K")
+    if not q_obs.is_contiguous():
+        raise ValueError("q_obs must be contiguous")
+    if K.stride(2) != 1:
+        raise ValueError("K/V last dimension must be contiguous")
+    if cu_seqlens is None:
+        if B != 1:
+            raise ValueError("cu_seqlens is required for batch > 1")
+        cu_seqlens = [0, T]
+    cu = np.asarray(cu_seqlens.cpu() if torch.is_tensor(cu_seqlens) else cu_seqlens, dtype=np.int64)
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal K.shape[1]")
+    return Spec(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, obs_window=obs_window,
+                pool_kernel=pool_kernel, ratio=ratio, budget=budget, dtype=_dtype_code(K), cu_seqlens=cu,
+                kv_head_stride=K.stride(0), kv_token_stride=K.stride(1), variant=variant, two_pass=two_pass)
+
+
+def workspace(spec: Spec, device) -> torch.Tensor:
+    ws = torch.empty(spec.ws_bytes, dtype=torch.uint8, device=device)
+    if ws.data_ptr() % 256:
+        raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
+    return ws
+
+
+def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
+           variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None):
+    """snapkv_scores: returns (votes or None, pooled), float32 [H_kv, sum_P]."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
+    dev = K.device
+    votes = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev) if want_votes else None
+    pooled = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = workspace(spec, dev)
+    st = load().snapkv_scores(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(votes), _ptr(pooled),
+                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st, "snapkv_scores")
+    return votes, pooled
+
+
+def select(pooled, q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
+           ws=None):
+    """snapkv_select over a given pooled vote: returns idx int32 [H_kv, sum_k]."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget)
+    if pooled.dtype != torch.float32 or tuple(pooled.shape) != (spec.Hkv, spec.sum_P) or not pooled.is_contiguous():
+        raise ValueError("pooled must be contiguous float32 [H_kv, sum_P]")
+    idx = torch.empty((spec.Hkv, spec.sum_k), dtype=torch.int32, device=K.device)
+    if ws is None:
+        ws = workspace(spec, K.device)
+    st = load().snapkv_select(ctypes.byref(spec.pb), _ptr(pooled), _ptr(idx), _ptr(ws),
+                              ctypes.c_size_t(ws.numel()), _stream())
+    _check(st, "snapkv_select")
+    return idx
+
+
+def gather(K, V, idx, q_obs, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None):
+    """snapkv_gather: returns (K_out, V_out) [H_kv, sum_out, d]."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget)
+    if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
+        raise ValueError("V must match K in shape, strides and dtype")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (spec.Hkv, spec.sum_k) or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [H_kv, sum_k]")
+    K_out = torch.empty((spec.Hkv, spec.sum_out, spec.head_dim), dtype=K.dtype, device=K.device)
+    V_out = torch.empty_like(K_out)
+    st = load().snapkv_gather(ctypes.byref(spec.pb), _ptr(K), _ptr(V), _ptr(idx), _ptr(K_out), _ptr(V_out),
+                              _stream())
+    _check(st, "snapkv_gather")
+    return K_out, V_out
+
+
+def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
+             variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None):
+    """snapkv_compress: the whole path.
+
+    Returns dict(K_out, V_out [H_kv, sum_out, d], idx int32 [H_kv, sum_k], cu_out int64 [B+1], k int64 [B],
+    pooled float32 [H_kv, sum_P] if want_pooled).  Defaults follow the pages' listing
+    (obs_window=32, kernel=7); exactly one of ratio and budget must be given.
+    """
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
+    if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
+        raise ValueError("V must match K in shape, strides and dtype")
+    dev = K.device
+    if out is None:
+        K_out = torch.empty((spec.Hkv, spec.sum_out, spec.head_dim), dtype=K.dtype, device=dev)
+        V_out = torch.empty_like(K_out)
+        idx = torch.empty((spec.Hkv, spec.sum_k), dtype=torch.int32, device=dev)
+        pooled = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev) if want_pooled else None
+    else:
+        K_out, V_out, idx, pooled = out["K_out"], out["V_out"], out["idx"], out.get("pooled")
+    if ws is None:
+        ws = workspace(spec, dev)
+    st = load().snapkv_compress(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(V), _ptr(K_out), _ptr(V_out),
+                                _ptr(idx), _ptr(pooled), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+    _check(st, "snapkv_compress")
+    res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy())
+    if pooled is not None:
+        res["pooled"] = pooled
+    return res

@@ -1,0 +1,514 @@
+// api.hip -- host side of libsnapkv: validation, planning, workspace layout, launches.
+//
+// Every argument check runs here before the first launch, so an invalid call writes
+// nothing.  The per-request table travels as a kernel argument; batches larger than
+// kMaxReq requests run as several groups of launches on the same stream.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "snapkv.h"
+#include "snapkv_internal.h"
+
+using namespace snapkv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+constexpr size_t kWsAlign = 256;
+constexpr uint32_t kSpinLimit = 1u << 26;  // polls of a barrier counter before giving up (seconds)
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct Group {
+    ReqTable rt;
+    int n_slabs;       // slabs of all KV heads of the group's requests
+    int max_ns;        // largest slab count of one (request, KV head)
+    int max_P;         // largest prefix in the group
+    int64_t out_rows;  // output rows of the group per KV head
+};
+
+struct Plan {
+    int B, Hq, Hkv, d, w, K_pool, mode, dtype, variant;
+    uint32_t flags;
+    int G, M, M_pad, esz, row_bytes;
+    double ratio;
+    int64_t budget, head_stride, token_stride;
+    std::vector<int64_t> L, P, k, cu_pfx, cu_k, cu_out;
+    int64_t sum_P, sum_k, sum_out;
+    ObsConfig cfg;
+    std::vector<Group> groups;
+    int max_group_slabs, max_group_segs;
+    // workspace layout (bytes)
+    size_t off_err, off_cnt, off_partial, off_merged, off_votes, off_pooled, off_idx, ws_bytes;
+};
+
+int make_plan(const snapkv_problem *pb, Plan *pl) {
+    g_last_error.clear();
+    if (!pb) return fail(SNAPKV_EINVAL, "problem is NULL");
+    Plan &p = *pl;
+    p.B = pb->batch;
+    p.Hq = pb->num_q_heads;
+    p.Hkv = pb->num_kv_heads;
+    p.d = pb->head_dim;
+    p.w = pb->obs_window;
+    p.K_pool = pb->pool_kernel;
+    p.mode = pb->mode;
+    p.dtype = pb->dtype;
+    p.variant = pb->variant;
+    p.flags = pb->flags;
+    p.ratio = pb->ratio;
+    p.budget = pb->budget;
+    p.head_stride = pb->kv_head_stride;
+    p.token_stride = pb->kv_token_stride;
+    if (p.B < 1) return fail(SNAPKV_EINVAL, "batch must be >= 1");
+    if (p.Hq < 1 || p.Hkv < 1) return fail(SNAPKV_EINVAL, "head counts must be >= 1");
+    if (p.Hq % p.Hkv != 0) return fail(SNAPKV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+    if (p.w < 1) return fail(SNAPKV_EINVAL, "obs_window must be >= 1");
+    if (p.K_pool < 1 || p.K_pool % 2 == 0) return fail(SNAPKV_EINVAL, "pool_kernel must be odd and >= 1");
+    if (p.mode != SNAPKV_RATIO && p.mode != SNAPKV_BUDGET) return fail(SNAPKV_EINVAL, "mode must be RATIO or BUDGET");
+    if (p.dtype != SNAPKV_F32 && p.dtype != SNAPKV_BF16) return fail(SNAPKV_EINVAL, "dtype must be F32 or BF16");
+    if (p.variant != SNAPKV_CAUSAL_WINDOW && p.variant != SNAPKV_PREFIX_ONLY)
+        return fail(SNAPKV_EINVAL, "variant must be CAUSAL_WINDOW or PREFIX_ONLY");
+    if (p.flags & ~SNAPKV_FLAG_TWO_PASS) return fail(SNAPKV_EINVAL, "unknown flag bits");
+    if (p.mode == SNAPKV_RATIO && !(p.ratio > 0.0 && p.ratio <= 1.0))
+        return fail(SNAPKV_EINVAL, "ratio must lie in (0, 1]");
+    if (p.mode == SNAPKV_BUDGET && p.budget < 0) return fail(SNAPKV_EINVAL, "budget must be >= 0");
+    if (!pb->cu_seqlens_host) return fail(SNAPKV_EINVAL, "cu_seqlens_host is NULL");
+    if (p.d != 64 && p.d != 128) return fail(SNAPKV_EUNSUPPORTED, "head_dim must be 64 or 128");
+    p.G = p.Hq / p.Hkv;
+    const int64_t M = (int64_t)p.G * p.w;
+    if (M > 256) return fail(SNAPKV_EUNSUPPORTED, "G * obs_window must be <= 256");
+    p.M = (int)M;
+    p.M_pad = (p.M + 15) / 16 * 16;
+    if (!obs_config(p.dtype, p.d, p.M_pad, &p.cfg)) return fail(SNAPKV_EUNSUPPORTED, "no kernel for this shape");
+    p.esz = p.dtype == SNAPKV_F32 ? 4 : 2;
+    p.row_bytes = p.d * p.esz;
+    if (p.token_stride < p.d) return fail(SNAPKV_EINVAL, "kv_token_stride must be >= head_dim");
+    if (p.head_stride < 0) return fail(SNAPKV_EINVAL, "kv_head_stride must be >= 0");
+    if ((p.token_stride * p.esz) % 16 || (p.head_stride * p.esz) % 16)
+        return fail(SNAPKV_EINVAL, "K/V strides must keep rows 16-byte aligned");
+
+    const int32_t *cu = pb->cu_seqlens_host;
+    if (cu[0] != 0) return fail(SNAPKV_EINVAL, "cu_seqlens[0] must be 0");
+    p.L.resize(p.B);
+    p.P.resize(p.B);
+    p.k.resize(p.B);
+    p.cu_pfx.assign(p.B + 1, 0);
+    p.cu_k.assign(p.B + 1, 0);
+    p.cu_out.assign(p.B + 1, 0);
+    for (int r = 0; r < p.B; ++r) {
+        const int64_t L = (int64_t)cu[r + 1] - cu[r];
+        if (L < p.w) return fail(SNAPKV_EINVAL, "request " + std::to_string(r) + " is shorter than obs_window");
+        const int64_t P = L - p.w;
+        int64_t k;
+        if (p.mode == SNAPKV_RATIO) {
+            k = (int64_t)floor(p.ratio * (double)P);
+            if (k > P) k = P;
+            if (k < 0) k = 0;
+        } else {
+            k = p.budget < P ? p.budget : P;
+        }
+        p.L[r] = L;
+        p.P[r] = P;
+        p.k[r] = k;
+        p.cu_pfx[r + 1] = p.cu_pfx[r] + P;
+        p.cu_k[r + 1] = p.cu_k[r] + k;
+        p.cu_out[r + 1] = p.cu_out[r] + k + p.w;
+    }
+    p.sum_P = p.cu_pfx[p.B];
+    p.sum_k = p.cu_k[p.B];
+    p.sum_out = p.cu_out[p.B];
+
+    // groups of at most kMaxReq requests
+    const int slab = p.cfg.slab_keys();
+    p.groups.clear();
+    p.max_group_slabs = 0;
+    p.max_group_segs = 0;
+    for (int r0 = 0; r0 < p.B; r0 += kMaxReq) {
+        Group gr;
+        memset(&gr, 0, sizeof gr);
+        const int n = p.B - r0 < kMaxReq ? p.B - r0 : kMaxReq;
+        gr.rt.n = n;
+        int64_t slabs = 0;
+        for (int i = 0; i < n; ++i) {
+            const int r = r0 + i;
+            gr.rt.L[i] = (int32_t)p.L[r];
+            gr.rt.k[i] = (int32_t)p.k[r];
+            gr.rt.qi[i] = r;
+            gr.rt.slab0[i] = (int32_t)slabs;
+            gr.rt.tok0[i] = cu[r];
+            gr.rt.pfx0[i] = p.cu_pfx[r];
+            gr.rt.k0[i] = p.cu_k[r];
+            gr.rt.out0[i] = p.cu_out[r];
+            const int64_t ns = (p.L[r] + slab - 1) / slab;
+            slabs += ns * p.Hkv;
+            if (ns > gr.max_ns) gr.max_ns = (int)ns;
+            if (p.P[r] > gr.max_P) gr.max_P = (int)p.P[r];
+        }
+        if (slabs > (1 << 30)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
+        gr.rt.slab0[n] = (int32_t)slabs;
+        gr.n_slabs = (int)slabs;
+        gr.out_rows = p.cu_out[r0 + n] - p.cu_out[r0];
+        p.groups.push_back(gr);
+        if (gr.n_slabs > p.max_group_slabs) p.max_group_slabs = gr.n_slabs;
+        if (n * p.Hkv > p.max_group_segs) p.max_group_segs = n * p.Hkv;
+    }
+    for (int r = 0; r < p.B; ++r)
+        if (cu[r + 1] > 0x7fffffff - 1) return fail(SNAPKV_EUNSUPPORTED, "token count exceeds int32");
+
+    // workspace: [err | counters] [partial] [merged] [votes] [pooled] [idx]
+    size_t off = 0;
+    p.off_err = off;
+    p.off_cnt = off + sizeof(uint32_t);
+    off = align_up(sizeof(uint32_t) * (1 + (size_t)p.max_group_segs));
+    p.off_partial = off;
+    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_slabs * p.M_pad);
+    p.off_merged = off;
+    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_segs * p.M_pad);
+    p.off_votes = off;
+    off = align_up(off + sizeof(float) * (size_t)p.Hkv * (size_t)p.sum_P);
+    p.off_pooled = off;
+    off = align_up(off + sizeof(float) * (size_t)p.Hkv * (size_t)p.sum_P);
+    p.off_idx = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)p.Hkv * (size_t)p.sum_k);
+    p.ws_bytes = off;
+    return SNAPKV_OK;
+}
+
+// ---- device facts (cached per device) ----
+
+struct DevInfo {
+    bool init = false;
+    int status = SNAPKV_OK;
+    int cus = 0;
+    bool coop = false;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+int device_info(DevInfo *out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SNAPKV_EHIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(SNAPKV_EUNSUPPORTED, "device ordinal out of range");
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    DevInfo &di = g_dev[dev];
+    if (!di.init) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(SNAPKV_EHIP, "hipGetDeviceProperties failed");
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            di.status = SNAPKV_EUNSUPPORTED;
+        } else {
+            di.cus = prop.multiProcessorCount;
+            int coop = 0;
+            if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
+            di.coop = coop != 0;
+        }
+        di.init = true;
+    }
+    *out = di;
+    if (di.status != SNAPKV_OK) return fail(di.status, "libsnapkv runs on gfx950 (MI355X) only");
+    return SNAPKV_OK;
+}
+
+int occupancy(const void *kernel, int threads) {
+    static std::mutex mu;
+    static std::vector<std::pair<const void *, int>> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lk(mu);
+    const void *key = (const char *)kernel + dev;  // kernels are distinct; device folded in
+    for (auto &e : cache)
+        if (e.first == key) return e.second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess) n = 0;
+    cache.emplace_back(key, n);
+    return n;
+}
+
+bool aligned16(const void *ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int check_ws(const Plan &p, void *ws, size_t ws_bytes) {
+    if (!ws) return fail(SNAPKV_EWORKSPACE, "workspace is NULL");
+    if ((uintptr_t)ws % kWsAlign) return fail(SNAPKV_EWORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < p.ws_bytes)
+        return fail(SNAPKV_EWORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) + " bytes");
+    return SNAPKV_OK;
+}
+
+int launch(const void *kernel, dim3 grid, dim3 block, void *arg, hipStream_t stream) {
+    void *args[] = {arg};
+    if (hipLaunchKernel(kernel, grid, block, args, 0, stream) != hipSuccess)
+        return fail(SNAPKV_EHIP, std::string("kernel launch failed: ") + hipGetErrorString(hipGetLastError()));
+    return SNAPKV_OK;
+}
+
+int fill_u32(uint32_t *ptr, int64_t n, uint32_t v, hipStream_t stream) {
+    FillParams fp{ptr, n, v};
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (blocks < 1) blocks = 1;
+    return launch(fill_kernel(), dim3((unsigned)blocks), dim3(256), &fp, stream);
+}
+
+// Scores of every group: votes (into `votes`) and pooled votes (into `pooled`).
+int run_scores(const Plan &p, const void *q, const void *K, float *votes, float *pooled, char *ws,
+               hipStream_t stream) {
+    DevInfo di;
+    int st = device_info(&di);
+    if (st) return st;
+    const ObsConfig &cfg = p.cfg;
+    const int slab = cfg.slab_keys();
+    uint32_t *err = (uint32_t *)(ws + p.off_err);
+    uint32_t *counters = (uint32_t *)(ws + p.off_cnt);
+    float2 *partial = (float2 *)(ws + p.off_partial);
+    float2 *merged = (float2 *)(ws + p.off_merged);
+    const void *kf = obs_kernel(p.dtype, p.d, p.M_pad, kFused);
+    const int occ = occupancy(kf, cfg.threads());
+    const int resident = occ * di.cus;
+    for (const Group &gr : p.groups) {
+        ObsParams op;
+        memset(&op, 0, sizeof op);
+        op.q = q;
+        op.K = K;
+        op.votes = votes;
+        op.partial = partial;
+        op.merged = merged;
+        op.counters = counters;
+        op.err = err;
+        op.head_stride = p.head_stride;
+        op.token_stride = p.token_stride;
+        op.sum_P = p.sum_P;
+        op.Hq = p.Hq;
+        op.Hkv = p.Hkv;
+        op.G = p.G;
+        op.w = p.w;
+        op.M = p.M;
+        op.M_pad = p.M_pad;
+        op.variant = p.variant;
+        op.c = (float)(1.4426950408889634 / sqrt((double)p.d));
+        op.n_slabs = gr.n_slabs;
+        op.slab_keys = slab;
+        op.spin_limit = kSpinLimit;
+        op.rt = gr.rt;
+        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && di.coop && resident > 0 && gr.max_ns <= resident;
+        const int n_seg = gr.rt.n * p.Hkv;
+        if (fused) {
+            st = fill_u32(err, 1 + (int64_t)n_seg, 0u, stream);  // error word and arrival counters
+            if (st) return st;
+            const int grid = gr.n_slabs < resident ? gr.n_slabs : resident;
+            void *args[] = {&op};
+            if (hipLaunchCooperativeKernel(kf, dim3(grid), dim3(cfg.threads()), args, 0, stream) != hipSuccess)
+                return fail(SNAPKV_EHIP, std::string("cooperative launch failed: ") + hipGetErrorString(hipGetLastError()));
+        } else {
+            st = fill_u32(err, 1, 0u, stream);
+            if (st) return st;
+            st = launch(obs_kernel(p.dtype, p.d, p.M_pad, kStats), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            if (st) return st;
+            MergeParams mp;
+            memset(&mp, 0, sizeof mp);
+            mp.partial = partial;
+            mp.merged = merged;
+            mp.M = p.M;
+            mp.M_pad = p.M_pad;
+            mp.slab_keys = slab;
+            mp.Hkv = p.Hkv;
+            mp.c = op.c;
+            mp.rt = gr.rt;
+            st = launch(merge_kernel(), dim3(n_seg), dim3(256), &mp, stream);
+            if (st) return st;
+            st = launch(obs_kernel(p.dtype, p.d, p.M_pad, kVotes), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            if (st) return st;
+        }
+        if (gr.max_P > 0) {
+            PoolParams pp;
+            memset(&pp, 0, sizeof pp);
+            pp.votes = votes;
+            pp.pooled = pooled;
+            pp.sum_P = p.sum_P;
+            pp.w = p.w;
+            pp.half = p.K_pool / 2;
+            pp.rt = gr.rt;
+            st = launch(pool_kernel(), dim3((gr.max_P + 255) / 256, gr.rt.n, p.Hkv), dim3(256), &pp, stream);
+            if (st) return st;
+        }
+    }
+    return SNAPKV_OK;
+}
+
+int run_select(const Plan &p, const float *pooled, int32_t *idx, hipStream_t stream) {
+    if (p.sum_k == 0) return SNAPKV_OK;
+    for (const Group &gr : p.groups) {
+        SelectParams sp;
+        memset(&sp, 0, sizeof sp);
+        sp.pooled = pooled;
+        sp.idx = idx;
+        sp.sum_P = p.sum_P;
+        sp.sum_k = p.sum_k;
+        sp.w = p.w;
+        sp.Hkv = p.Hkv;
+        sp.rt = gr.rt;
+        int st = launch(select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp, stream);
+        if (st) return st;
+    }
+    return SNAPKV_OK;
+}
+
+int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, void *K_out, void *V_out,
+               hipStream_t stream) {
+    for (const Group &gr : p.groups) {
+        GatherParams gp;
+        memset(&gp, 0, sizeof gp);
+        gp.K = K;
+        gp.V = V;
+        gp.idx = idx;
+        gp.K_out = K_out;
+        gp.V_out = V_out;
+        gp.head_stride = p.head_stride;
+        gp.token_stride = p.token_stride;
+        gp.sum_k = p.sum_k;
+        gp.sum_out = p.sum_out;
+        gp.row_bytes = p.row_bytes;
+        gp.esz = p.esz;
+        gp.w = p.w;
+        gp.Hkv = p.Hkv;
+        gp.rt = gr.rt;
+        const int rpb = 256 / (p.row_bytes / 16);
+        int64_t blocks = (gr.out_rows + rpb - 1) / rpb;
+        if (blocks > 65535) blocks = 65535;
+        if (blocks < 1) blocks = 1;
+        int st = launch(gather_kernel(), dim3((unsigned)blocks, p.Hkv), dim3(256), &gp, stream);
+        if (st) return st;
+    }
+    return SNAPKV_OK;
+}
+
+int check_ptr(const void *ptr, const char *name) {
+    if (!ptr) return fail(SNAPKV_EINVAL, std::string(name) + " is NULL");
+    if (!aligned16(ptr)) return fail(SNAPKV_EINVAL, std::string(name) + " must be 16-byte aligned");
+    return SNAPKV_OK;
+}
+
+int check_opt_ptr(const void *ptr, const char *name) { return ptr ? check_ptr(ptr, name) : SNAPKV_OK; }
+
+int finish(int st) {
+    if (st) return st;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(SNAPKV_EHIP, std::string("HIP error: ") + hipGetErrorString(e));
+    return SNAPKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host, int64_t *cu_k_host,
+                int64_t *cu_out_host, size_t *ws_bytes) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (st) return st;
+    for (int r = 0; r < p.B; ++r)
+        if (k_host) k_host[r] = p.k[r];
+    for (int r = 0; r <= p.B; ++r) {
+        if (cu_pfx_host) cu_pfx_host[r] = p.cu_pfx[r];
+        if (cu_k_host) cu_k_host[r] = p.cu_k[r];
+        if (cu_out_host) cu_out_host[r] = p.cu_out[r];
+    }
+    if (ws_bytes) *ws_bytes = p.ws_bytes;
+    return SNAPKV_OK;
+}
+
+int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, float *votes, float *pooled,
+                  void *ws, size_t ws_bytes, void *stream) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (!st) st = check_ptr(q_obs, "q_obs");
+    if (!st) st = check_ptr(K, "K");
+    if (!st) st = check_opt_ptr(votes, "votes");
+    if (!st) st = check_ptr(pooled, "pooled");
+    if (!st) st = check_ws(p, ws, ws_bytes);
+    if (st) return st;
+    char *w = (char *)ws;
+    float *v = votes ? votes : (float *)(w + p.off_votes);
+    return finish(run_scores(p, q_obs, K, v, pooled, w, (hipStream_t)stream));
+}
+
+int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, void *ws, size_t ws_bytes,
+                  void *stream) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (!st) st = check_ptr(pooled, "pooled");
+    if (!st) st = check_ptr(idx, "idx");
+    if (!st) st = check_ws(p, ws, ws_bytes);
+    if (st) return st;
+    DevInfo di;
+    st = device_info(&di);
+    if (st) return st;
+    return finish(run_select(p, pooled, idx, (hipStream_t)stream));
+}
+
+int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const int32_t *idx, void *K_out,
+                  void *V_out, void *stream) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (!st) st = check_ptr(K, "K");
+    if (!st) st = check_ptr(V, "V");
+    if (!st) st = check_ptr(idx, "idx");
+    if (!st) st = check_ptr(K_out, "K_out");
+    if (!st) st = check_ptr(V_out, "V_out");
+    if (st) return st;
+    DevInfo di;
+    st = device_info(&di);
+    if (st) return st;
+    return finish(run_gather(p, K, V, idx, K_out, V_out, (hipStream_t)stream));
+}
+
+int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
+                    void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (!st) st = check_ptr(q_obs, "q_obs");
+    if (!st) st = check_ptr(K, "K");
+    if (!st) st = check_ptr(V, "V");
+    if (!st) st = check_ptr(K_out, "K_out");
+    if (!st) st = check_ptr(V_out, "V_out");
+    if (!st) st = check_opt_ptr(idx, "idx");
+    if (!st) st = check_opt_ptr(pooled, "pooled");
+    if (!st) st = check_ws(p, ws, ws_bytes);
+    if (st) return st;
+    char *w = (char *)ws;
+    hipStream_t s = (hipStream_t)stream;
+    float *votes = (float *)(w + p.off_votes);
+    float *pl = pooled ? pooled : (float *)(w + p.off_pooled);
+    int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
+    st = run_scores(p, q_obs, K, votes, pl, w, s);
+    if (!st) st = run_select(p, pl, ix, s);
+    if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s);
+    return finish(st);
+}
+
+const char *snapkv_strerror(int status) {
+    switch (status) {
+        case SNAPKV_OK: return "success";
+        case SNAPKV_EINVAL: return "invalid argument";
+        case SNAPKV_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case SNAPKV_EUNSUPPORTED: return "unsupported problem or device";
+        case SNAPKV_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *snapkv_last_error(void) { return g_last_error.c_str(); }
+
+int snapkv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,482 @@
+// obs_score.hip -- window-query votes (obs_score) and the stats merge, gfx950.
+//
+// What is computed (page "論文解説: SnapKV — アテンションパターン観測によるKVキャッシュ圧縮",
+// section 投票メカニズム, and the アルゴリズム listing): for every KV head g of request r,
+// the M = G * L_obs window queries of the query heads sharing g score every key the row
+// may see, s = q . k / sqrt(d); each row is a softmax over its visible keys; the vote of
+// prefix position j is the sum of its weights over all M rows.
+//
+// How it maps to CDNA4:
+//   * A work unit ("slab") is one (request, KV head) segment's run of SLAB consecutive
+//     keys.  Logits S = Q K^T are a dense contraction of depth d, computed with
+//     v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32).  A = window
+//     queries (held in VGPRs for the whole slab), B = keys streamed from HBM straight
+//     into the MFMA operand layout, 16-byte loads, two key tiles in flight per wave.
+//   * The d-dimension of each lane's operand is permuted so that one load instruction
+//     covers 64 contiguous bytes of each of 16 key rows; A and B use the same
+//     permutation, so every dot product is unchanged.
+//   * kFused keeps the slab's logits in registers: per-row max and sum of exponentials
+//     over the slab are published, the slabs of a segment meet at a counter barrier
+//     (grid launched cooperatively, so all slabs of a segment are resident), each slab
+//     merges the segment's row stats and turns its resident logits into votes.  K is
+//     read from HBM once.
+//   * kStats / kVotes are the two-pass path for segments with more slabs than fit on
+//     the chip at once: first pass publishes stats, merge_kernel combines them, second
+//     pass recomputes the logits and writes votes.
+// Exponentials are base 2: s*log2(e)/sqrt(d) with the scale folded into one FMA.
+#include "snapkv_internal.h"
+
+namespace snapkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Dot;
+
+// One 16-byte operand chunk per lane = 8 bf16 = one 16x16x32 MFMA.
+template <>
+struct Dot<__bf16> {
+    __device__ static inline f32x4_t step(const u32x4_t &a, const u32x4_t &b, f32x4_t acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
+};
+
+// One 16-byte operand chunk per lane = 4 fp32 = four 16x16x4 MFMAs.  (Elements are read
+// with __uint_as_float(v[i]): a bit cast of a vector element expression reads element 0
+// with this compiler.)
+template <>
+struct Dot<float> {
+    __device__ static inline f32x4_t step(const u32x4_t &a, const u32x4_t &b, f32x4_t acc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+struct SlabPos {
+    int r, g, sl, ns;
+    int seg_slab0;  // first slab of the segment
+};
+
+__device__ inline SlabPos decode_slab(const ReqTable &rt, int s, int slab_keys) {
+    int r = 0;
+    while (r + 1 < rt.n && rt.slab0[r + 1] <= s) ++r;
+    SlabPos p;
+    p.r = r;
+    p.ns = (rt.L[r] + slab_keys - 1) / slab_keys;
+    const int local = s - rt.slab0[r];
+    p.g = local / p.ns;
+    p.sl = local - p.g * p.ns;
+    p.seg_slab0 = rt.slab0[r] + p.g * p.ns;
+    return p;
+}
+
+__device__ inline float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (m, l) pairs: l is a sum of exp2((s - m) * c).  Merge two of them.
+__device__ inline void merge_stats(float &m, float &l, float m2, float l2, float c) {
+    const float mx = fmaxf(m, m2);
+    if (mx == neg_inf()) return;  // both empty
+    const float a = (m == neg_inf()) ? 0.f : l * fast_exp2((m - mx) * c);
+    const float b = (m2 == neg_inf()) ? 0.f : l2 * fast_exp2((m2 - mx) * c);
+    m = mx;
+    l = a + b;
+}
+
+template <typename T, int D, int WR, int WK, int RTW, int CTW, int MODE>
+__global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams p) {
+    constexpr int NT = 64 * WR * WK;
+    constexpr int ESZ = (int)sizeof(T);
+    constexpr int ROWB = D * ESZ;       // bytes per key / query row
+    constexpr int NQ = ROWB / 64;       // 16-byte loads per lane per row
+    constexpr int SLAB = WK * CTW * 16; // keys per slab
+    constexpr int MROWS = WR * RTW * 16;
+    constexpr int PF = 2;               // key tiles in flight per wave
+    constexpr int NCH = ROWB / 16;      // 16-byte chunks per row
+    constexpr bool QLDS = WR == 1;      // window queries read from LDS
+    static_assert(ROWB % 64 == 0, "row must be a multiple of 64 bytes");
+    // LDS rows padded by one chunk so the 16 rows of an MFMA operand hit distinct banks
+    __shared__ u32x4_t sh_q[QLDS ? MROWS : 1][NCH + 1];
+
+    __shared__ float sh_m[WK][MROWS];
+    __shared__ float sh_l[WK][MROWS];
+    __shared__ float sh_rowm[MROWS];
+    __shared__ float sh_f[MROWS];
+    __shared__ float sh_v[WR][SLAB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WK, wk = wave - (wave / WK) * WK;
+    const int n16 = lane & 15, grp = lane >> 4;
+    const float c = p.c;
+
+    for (int s = blockIdx.x; s < p.n_slabs; s += gridDim.x) {
+        const SlabPos sp = decode_slab(p.rt, s, SLAB);
+        const int L = p.rt.L[sp.r];
+        const int P = L - p.w;
+        const int key0 = sp.sl * SLAB;
+        const int kw0 = key0 + wk * CTW * 16;  // first key of this wave
+        const int seg = sp.r * p.Hkv + sp.g;
+
+        // Window queries of the group: rows r*G*L_obs .. of q_obs, zero beyond M.  With one
+        // row wave (QLDS) they sit in LDS and are re-read per key tile, which frees the
+        // VGPRs the resident logits need; otherwise each wave keeps its rows in VGPRs.
+        const char *qb = (const char *)p.q +
+                         ((int64_t)p.rt.qi[sp.r] * p.Hq + (int64_t)sp.g * p.G) * (int64_t)p.w * ROWB;
+        u32x4_t qf[QLDS ? 1 : RTW][NQ];
+        if constexpr (QLDS) {
+            for (int e = tid; e < MROWS * NCH; e += NT) {
+                const int row = e / NCH, ch = e - (e / NCH) * NCH;
+                sh_q[row][ch] = row < p.M ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + ch * 16)
+                                          : u32x4_t{0u, 0u, 0u, 0u};
+            }
+            __syncthreads();
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                const int row = (wr * RTW + rt) * 16 + n16;
+#pragma unroll
+                for (int qq = 0; qq < NQ; ++qq) {
+                    if (row < p.M)
+                        qf[rt][qq] = *(const u32x4_t *)(qb + (int64_t)row * ROWB + (4 * qq + grp) * 16);
+                    else
+                        qf[rt][qq] = u32x4_t{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+
+        // Logits of this wave's CTW key tiles.
+        f32x4_t S[RTW][CTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct) S[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            const char *kb = (const char *)p.K +
+                             ((int64_t)sp.g * p.head_stride + p.rt.tok0[sp.r] * p.token_stride) * ESZ + grp * 16;
+            const int64_t tstride = p.token_stride * ESZ;
+            u32x4_t buf[PF][NQ];
+#pragma unroll
+            for (int f = 0; f < PF; ++f) {
+                if (f < CTW && kw0 + f * 16 < L) {
+                    int j = kw0 + f * 16 + n16;
+                    j = j < L ? j : L - 1;
+                    const char *a = kb + (int64_t)j * tstride;
+#pragma unroll
+                    for (int qq = 0; qq < NQ; ++qq) buf[f][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct) {
+                if (kw0 + ct * 16 < L) {
+                    u32x4_t cur[NQ];
+#pragma unroll
+                    for (int qq = 0; qq < NQ; ++qq) cur[qq] = buf[ct % PF][qq];
+                    if (ct + PF < CTW && kw0 + (ct + PF) * 16 < L) {
+                        int j = kw0 + (ct + PF) * 16 + n16;
+                        j = j < L ? j : L - 1;
+                        const char *a = kb + (int64_t)j * tstride;
+#pragma unroll
+                        for (int qq = 0; qq < NQ; ++qq)
+                            buf[ct % PF][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
+                    }
+                    if constexpr (QLDS) {
+                        // keep the compiler from merging the per-tile LDS reads into registers
+                        asm volatile("" ::: "memory");
+#pragma unroll
+                        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                            for (int qq = 0; qq < NQ; ++qq)
+                                S[rt][ct] = Dot<T>::step(sh_q[rt * 16 + n16][4 * qq + grp], cur[qq], S[rt][ct]);
+                    } else {
+#pragma unroll
+                        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                            for (int qq = 0; qq < NQ; ++qq) S[rt][ct] = Dot<T>::step(qf[rt][qq], cur[qq], S[rt][ct]);
+                    }
+                }
+            }
+        }
+
+        // Mask keys a row may not see: beyond the request, or (causal window) window keys
+        // after the row's own position, or (prefix-only variant) every window key.
+        if (key0 + SLAB > P) {
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
+                    const int lim = p.variant == 0 ? P + row % p.w + 1 : P;  // keys j < lim are visible
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) {
+                        const int j = kw0 + ct * 16 + n16;
+                        if (j >= lim) S[rt][ct][i] = neg_inf();
+                    }
+                }
+        }
+
+        if constexpr (MODE == kFused || MODE == kStats) {
+            // Row max over the slab.
+            float mrow[RTW][4];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float m = S[rt][0][i];
+#pragma unroll
+                    for (int ct = 1; ct < CTW; ++ct) m = fmaxf(m, S[rt][ct][i]);
+                    m = fmaxf(m, __shfl_xor(m, 1, 16));
+                    m = fmaxf(m, __shfl_xor(m, 2, 16));
+                    m = fmaxf(m, __shfl_xor(m, 4, 16));
+                    m = fmaxf(m, __shfl_xor(m, 8, 16));
+                    mrow[rt][i] = m;
+                }
+            if constexpr (WK > 1) {
+                if (n16 == 0)
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sh_m[wk][(wr * RTW + rt) * 16 + 4 * grp + i] = mrow[rt][i];
+                __syncthreads();
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
+                        float m = sh_m[0][row];
+#pragma unroll
+                        for (int k2 = 1; k2 < WK; ++k2) m = fmaxf(m, sh_m[k2][row]);
+                        mrow[rt][i] = m;
+                    }
+            }
+            // Exponentials in place and row sums.
+            float lrow[RTW][4];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sh = mrow[rt][i] == neg_inf() ? 0.f : mrow[rt][i] * c;
+                    float l = 0.f;
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) {
+                        const float e = fast_exp2(fmaf(S[rt][ct][i], c, -sh));
+                        S[rt][ct][i] = e;
+                        l += e;
+                    }
+                    l += __shfl_xor(l, 1, 16);
+                    l += __shfl_xor(l, 2, 16);
+                    l += __shfl_xor(l, 4, 16);
+                    l += __shfl_xor(l, 8, 16);
+                    lrow[rt][i] = l;
+                }
+            if constexpr (WK > 1) {
+                if (n16 == 0)
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sh_l[wk][(wr * RTW + rt) * 16 + 4 * grp + i] = lrow[rt][i];
+                __syncthreads();
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
+                        float l = sh_l[0][row];
+#pragma unroll
+                        for (int k2 = 1; k2 < WK; ++k2) l += sh_l[k2][row];
+                        lrow[rt][i] = l;
+                    }
+            }
+            if (wk == 0 && n16 == 0) {
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
+                        if (row < p.M) p.partial[(int64_t)s * p.M_pad + row] = make_float2(mrow[rt][i], lrow[rt][i]);
+                        sh_rowm[row] = mrow[rt][i];
+                    }
+            }
+        }
+
+        if constexpr (MODE == kStats) {
+            __syncthreads();
+            continue;
+        }
+
+        if constexpr (MODE == kFused) {
+            // All slabs of the segment publish, then meet.  Every slab publishes before it
+            // waits, and a segment never has more slabs than resident workgroups, so the
+            // wait ends; a poll limit turns a broken launch into an error bit instead of a hang.
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) {
+                atomicAdd(&p.counters[seg], 1u);
+                uint32_t spins = 0;
+                while (__hip_atomic_load(&p.counters[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                       (uint32_t)sp.ns) {
+                    __builtin_amdgcn_s_sleep(2);
+                    if (++spins > p.spin_limit) {
+                        atomicOr(p.err, 1u);
+                        break;
+                    }
+                }
+            }
+            __syncthreads();
+            __threadfence();
+            // Merge the segment's row stats; factor for this slab's resident weights.
+            constexpr int TPR = NT / MROWS;  // threads per row (power of two)
+            const int row = tid / TPR, sub = tid - (tid / TPR) * TPR;
+            float mm = neg_inf(), ll = 0.f;
+            if (row < p.M) {
+                for (int s2 = sub; s2 < sp.ns; s2 += TPR) {
+                    const float2 pr = p.partial[(int64_t)(sp.seg_slab0 + s2) * p.M_pad + row];
+                    merge_stats(mm, ll, pr.x, pr.y, c);
+                }
+            }
+#pragma unroll
+            for (int o = 1; o < TPR; o <<= 1) {
+                const float m2 = __shfl_xor(mm, o, TPR);
+                const float l2 = __shfl_xor(ll, o, TPR);
+                merge_stats(mm, ll, m2, l2, c);
+            }
+            if (sub == 0) {
+                const float rm = sh_rowm[row];
+                sh_f[row] = (row < p.M && rm != neg_inf() && ll > 0.f) ? fast_exp2((rm - mm) * c) / ll : 0.f;
+            }
+            __syncthreads();
+        }
+
+        if constexpr (MODE == kVotes) {
+            if (tid < MROWS) {
+                const int row = tid;
+                float2 mg = make_float2(0.f, 0.f);
+                if (row < p.M) mg = p.merged[(int64_t)seg * p.M_pad + row];
+                const bool ok = row < p.M && mg.x != neg_inf() && mg.y > 0.f;
+                sh_rowm[row] = ok ? mg.x : 0.f;
+                sh_f[row] = ok ? 1.f / mg.y : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sh = sh_rowm[(wr * RTW + rt) * 16 + 4 * grp + i] * c;
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) S[rt][ct][i] = fast_exp2(fmaf(S[rt][ct][i], c, -sh));
+                }
+        }
+
+        // Votes: weight * row factor, summed over this wave's rows, the four row groups of
+        // the MFMA layout, then the row waves.
+        {
+            float f[RTW][4];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp + i];
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct) {
+                float v = 0.f;
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v = fmaf(S[rt][ct][i], f[rt][i], v);
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (grp == 0) sh_v[wr][(wk * CTW + ct) * 16 + n16] = v;
+            }
+            __syncthreads();
+            float *vout = p.votes + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
+            for (int t = tid; t < SLAB; t += NT) {
+                const int j = key0 + t;
+                if (j < P) {
+                    float a = sh_v[0][t];
+#pragma unroll
+                    for (int w2 = 1; w2 < WR; ++w2) a += sh_v[w2][t];
+                    vout[j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Two-pass path: combine the per-slab stats of every (request, KV head, row).
+__global__ void __launch_bounds__(256) merge_stats_kernel(const MergeParams p) {
+    const int seg = blockIdx.x;
+    const int r = seg / p.Hkv, g = seg - (seg / p.Hkv) * p.Hkv;
+    const int ns = (p.rt.L[r] + p.slab_keys - 1) / p.slab_keys;
+    const int base = p.rt.slab0[r] + g * ns;
+    for (int row = threadIdx.x; row < p.M; row += blockDim.x) {
+        float m = neg_inf(), l = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float2 pr = p.partial[(int64_t)(base + s) * p.M_pad + row];
+            merge_stats(m, l, pr.x, pr.y, p.c);
+        }
+        p.merged[(int64_t)seg * p.M_pad + row] = make_float2(m, l);
+    }
+}
+
+const void *merge_kernel() { return (const void *)&merge_stats_kernel; }
+
+// ---- instantiation table ---------------------------------------------------------------
+
+bool obs_config(int dtype, int d, int m_pad, ObsConfig *cfg) {
+    if (d != 64 && d != 128) return false;
+    const int rowb = d * (dtype == 0 ? 4 : 2);
+    ObsConfig c;
+    if (rowb <= 256) {
+        if (m_pad <= 32) c = {1, 8, 2, 16};
+        else if (m_pad <= 64) c = {1, 8, 4, 8};
+        else if (m_pad <= 128) c = {2, 4, 4, 8};
+        else if (m_pad <= 256) c = {4, 2, 4, 8};
+        else return false;
+    } else {
+        if (m_pad <= 32) c = {1, 8, 2, 8};
+        else if (m_pad <= 64) c = {2, 4, 2, 8};
+        else if (m_pad <= 128) c = {4, 2, 2, 8};
+        else if (m_pad <= 256) c = {8, 1, 2, 8};
+        else return false;
+    }
+    *cfg = c;
+    return true;
+}
+
+template <typename T, int D, int WR, int WK, int RTW, int CTW>
+static const void *pick_mode(int mode) {
+    switch (mode) {
+        case kFused: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kFused>;
+        case kStats: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kStats>;
+        default: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kVotes>;
+    }
+}
+
+template <typename T, int D>
+static const void *pick_small_rows(int m_pad, int mode) {  // rows of D*sizeof(T) <= 256 bytes
+    if (m_pad <= 32) return pick_mode<T, D, 1, 8, 2, 16>(mode);
+    if (m_pad <= 64) return pick_mode<T, D, 1, 8, 4, 8>(mode);
+    if (m_pad <= 128) return pick_mode<T, D, 2, 4, 4, 8>(mode);
+    return pick_mode<T, D, 4, 2, 4, 8>(mode);
+}
+
+static const void *pick_f32_d128(int m_pad, int mode) {
+    if (m_pad <= 32) return pick_mode<float, 128, 1, 8, 2, 8>(mode);
+    if (m_pad <= 64) return pick_mode<float, 128, 2, 4, 2, 8>(mode);
+    if (m_pad <= 128) return pick_mode<float, 128, 4, 2, 2, 8>(mode);
+    return pick_mode<float, 128, 8, 1, 2, 8>(mode);
+}
+
+const void *obs_kernel(int dtype, int d, int m_pad, int mode) {
+    if (m_pad > 256) return nullptr;
+    if (dtype == 1) return d == 64 ? pick_small_rows<__bf16, 64>(m_pad, mode) : pick_small_rows<__bf16, 128>(m_pad, mode);
+    return d == 64 ? pick_small_rows<float, 64>(m_pad, mode) : pick_f32_d128(m_pad, mode);
+}
+
+}  // namespace snapkv

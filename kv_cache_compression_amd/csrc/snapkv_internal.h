@@ -1,0 +1,109 @@
+// snapkv_internal.h -- shared between the host API and the gfx950 kernels of libsnapkv.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace snapkv {
+
+// Requests handled by one group of launches.  Larger batches are cut into
+// groups; the per-request table travels as a kernel argument (no copies).
+constexpr int kMaxReq = 32;
+
+struct ReqTable {
+    int32_t n;                    // requests in this group
+    int32_t L[kMaxReq];           // request length
+    int32_t k[kMaxReq];           // kept prefix positions
+    int32_t qi[kMaxReq];          // request index into q_obs
+    int32_t slab0[kMaxReq + 1];   // first slab of the request (all KV heads), cumulative
+    int64_t tok0[kMaxReq];        // first token in K/V
+    int64_t pfx0[kMaxReq];        // first column in votes/pooled
+    int64_t k0[kMaxReq];          // first column in idx
+    int64_t out0[kMaxReq];        // first row in K_out/V_out
+};
+
+// Scoring kernel modes.
+enum ObsMode : int {
+    kFused = 0,   // logits stay in registers: local stats, per-segment barrier, votes
+    kStats = 1,   // first pass of the two-pass path: per-slab (max, sum-exp)
+    kVotes = 2    // second pass: logits again, normalised by merged stats
+};
+
+struct ObsParams {
+    const void *q;              // q_obs
+    const void *K;
+    float *votes;               // [H_kv][sum_P]
+    float2 *partial;            // [slabs][M_pad]: (max of raw logits, sum of exp2((s-max)*c))
+    const float2 *merged;       // [segments][M_pad]: merged (max, sum) for kVotes
+    uint32_t *counters;         // [segments] arrival counters for kFused
+    uint32_t *err;              // error word (bit 0: a barrier wait gave up)
+    int64_t head_stride;        // elements
+    int64_t token_stride;       // elements
+    int64_t sum_P;
+    int32_t Hq, Hkv, G, w, M, M_pad, variant;
+    float c;                    // log2(e) / sqrt(d)
+    int32_t n_slabs;            // slabs in this group
+    int32_t slab_keys;          // keys per slab
+    uint32_t spin_limit;        // polls before a barrier wait gives up
+    ReqTable rt;
+};
+
+struct ObsConfig {
+    int wr, wk, rtw, ctw;       // waves over rows, waves over keys, 16-row tiles / wave, 16-key tiles / wave
+    int threads() const { return 64 * wr * wk; }
+    int slab_keys() const { return wk * ctw * 16; }
+    int rows() const { return wr * rtw * 16; }
+};
+
+// Chooses the tile shape for (dtype, d, rows); false if unsupported.
+bool obs_config(int dtype, int d, int m_pad, ObsConfig *cfg);
+// Kernel entry of the chosen instantiation.
+const void *obs_kernel(int dtype, int d, int m_pad, int mode);
+
+struct MergeParams {
+    const float2 *partial;
+    float2 *merged;
+    int32_t M, M_pad, slab_keys, Hkv;
+    float c;
+    ReqTable rt;
+};
+const void *merge_kernel();
+
+struct PoolParams {
+    const float *votes;
+    float *pooled;
+    int64_t sum_P;
+    int32_t w, half;            // half = K_pool / 2
+    ReqTable rt;
+};
+const void *pool_kernel();
+
+struct SelectParams {
+    const float *pooled;
+    int32_t *idx;
+    int64_t sum_P, sum_k;
+    int32_t w, Hkv;
+    ReqTable rt;
+};
+const void *select_kernel();
+int select_threads();
+
+struct GatherParams {
+    const void *K, *V;
+    const int32_t *idx;
+    void *K_out, *V_out;
+    int64_t head_stride, token_stride;  // elements of the input
+    int64_t sum_k, sum_out;
+    int32_t row_bytes, esz, w, Hkv;
+    ReqTable rt;
+};
+const void *gather_kernel();
+
+struct FillParams {
+    uint32_t *p;
+    int64_t n;
+    uint32_t v;
+};
+const void *fill_kernel();
+
+}  // namespace snapkv
