@@ -106,8 +106,13 @@ typedef struct {
  *   cu_k_host   [B+1] : exclusive prefix sums of k_r (idx offsets).
  *   cu_out_host [B+1] : exclusive prefix sums of k_r + L_obs (K_out/V_out rows).
  *   ws_bytes          : workspace bytes that snapkv_scores, snapkv_select and
- *                       snapkv_compress need for this problem on the current
- *                       device (0 is never returned).
+ *                       snapkv_compress need for this problem (device
+ *                       independent; 0 is never returned).
+ * Workspace contents: after a scoring call completes on its stream, the first
+ * 4 bytes hold an error word: 0 = fine; bit 0 set = a per-segment barrier gave
+ * up waiting (only possible if other work kept part of the scoring grid off
+ * the GPU for about a second); the outputs of that call are then invalid and
+ * SNAPKV_FLAG_TWO_PASS, which has no barrier, computes them.
  * Returns SNAPKV_OK or SNAPKV_EINVAL / SNAPKV_EUNSUPPORTED.
  */
 int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host, int64_t *cu_k_host,
@@ -150,6 +155,35 @@ int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const 
  */
 int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
                     void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Kernel trace (profiling hook).  While a trace is open on the calling thread,
+ * the i-th kernel a snapkv_* call launches (i < n_pairs) carries events[2i] and
+ * events[2i+1] as the start and stop events of its dispatch
+ * (hipExtLaunchKernel), so their elapsed time is that kernel's own duration on
+ * the launch stream; later launches are not recorded.  The events are the
+ * caller's hipEvent_t handles, created with timing enabled.
+ *   snapkv_trace_begin: opens a trace (events non-NULL, n_pairs >= 1).
+ *   snapkv_trace_end  : closes it, writes the snapkv_kernel_id of each recorded
+ *                       launch into kernel_ids[0 .. min(count, capacity)) and
+ *                       returns count (>= 0).
+ */
+typedef enum {
+    SNAPKV_K_FILL = 0,        /* zero the error word and barrier counters */
+    SNAPKV_K_OBS_FUSED = 1,   /* obs_score, logits resident, one read of K */
+    SNAPKV_K_OBS_STATS = 2,   /* obs_score two-pass: row stats */
+    SNAPKV_K_STATS_MERGE = 3, /* obs_score two-pass: merge of row stats */
+    SNAPKV_K_OBS_VOTES = 4,   /* obs_score two-pass: votes */
+    SNAPKV_K_POOL = 5,        /* vote_pool */
+    SNAPKV_K_SELECT = 6,      /* topk_select */
+    SNAPKV_K_GATHER = 7       /* kv_gather */
+} snapkv_kernel_id;
+
+int snapkv_trace_begin(void *const *events, int n_pairs);
+int snapkv_trace_end(int32_t *kernel_ids, int capacity);
+
+/* Name of a snapkv_kernel_id ("obs_score_fused", ...); never NULL. */
+const char *snapkv_kernel_name(int id);
 
 /* Text of a status code; never NULL. */
 const char *snapkv_strerror(int status);

@@ -24,6 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
+           "snapkv_trace_begin", "snapkv_trace_end", "snapkv_kernel_name",
            "snapkv_strerror", "snapkv_last_error", "snapkv_version")
 
 
@@ -81,6 +82,12 @@ def load() -> ctypes.CDLL:
             lib.snapkv_last_error.argtypes = []
             lib.snapkv_last_error.restype = ctypes.c_char_p
             lib.snapkv_version.restype = ctypes.c_int
+            lib.snapkv_trace_begin.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+            lib.snapkv_trace_begin.restype = ctypes.c_int
+            lib.snapkv_trace_end.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.c_int]
+            lib.snapkv_trace_end.restype = ctypes.c_int
+            lib.snapkv_kernel_name.argtypes = [ctypes.c_int]
+            lib.snapkv_kernel_name.restype = ctypes.c_char_p
             _lib = lib
     return _lib
 

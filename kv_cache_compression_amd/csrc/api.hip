@@ -10,6 +10,8 @@
 #include <string>
 #include <vector>
 
+#include <hip/hip_ext.h>
+
 #include "snapkv.h"
 #include "snapkv_internal.h"
 
@@ -25,7 +27,7 @@ int fail(int code, const std::string &msg) {
 }
 
 constexpr size_t kWsAlign = 256;
-constexpr uint32_t kSpinLimit = 1u << 26;  // polls of a barrier counter before giving up (seconds)
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls of a barrier counter before giving up (~1 s)
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
@@ -48,6 +50,7 @@ struct Plan {
     ObsConfig cfg;
     std::vector<Group> groups;
     int max_group_slabs, max_group_segs;
+    int64_t max_P;
     // workspace layout (bytes)
     size_t off_err, off_cnt, off_partial, off_merged, off_votes, off_pooled, off_idx, ws_bytes;
 };
@@ -126,6 +129,8 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
         p.cu_out[r + 1] = p.cu_out[r] + k + p.w;
     }
     p.sum_P = p.cu_pfx[p.B];
+    p.max_P = 0;
+    for (int r = 0; r < p.B; ++r) p.max_P = p.P[r] > p.max_P ? p.P[r] : p.max_P;
     p.sum_k = p.cu_k[p.B];
     p.sum_out = p.cu_out[p.B];
 
@@ -191,7 +196,6 @@ struct DevInfo {
     bool init = false;
     int status = SNAPKV_OK;
     int cus = 0;
-    bool coop = false;
 };
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
@@ -209,9 +213,6 @@ int device_info(DevInfo *out) {
             di.status = SNAPKV_EUNSUPPORTED;
         } else {
             di.cus = prop.multiProcessorCount;
-            int coop = 0;
-            if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) coop = 0;
-            di.coop = coop != 0;
         }
         di.init = true;
     }
@@ -245,11 +246,35 @@ int check_ws(const Plan &p, void *ws, size_t ws_bytes) {
     return SNAPKV_OK;
 }
 
-int launch(const void *kernel, dim3 grid, dim3 block, void *arg, hipStream_t stream) {
+// ---- kernel trace: caller's events recorded around each launch (per thread) ----
+
+struct Trace {
+    void *const *events = nullptr;
+    int n_pairs = 0;
+    int count = 0;
+    int32_t ids[4096];
+};
+thread_local Trace g_trace;
+
+// Every kernel goes through hipExtLaunchKernel: when a trace is open its start/stop
+// events are stamped by the dispatch itself, so traced durations are the kernels' own.
+int launch_traced(int id, const void *kernel, dim3 grid, dim3 block, void *arg, hipStream_t stream) {
     void *args[] = {arg};
-    if (hipLaunchKernel(kernel, grid, block, args, 0, stream) != hipSuccess)
+    Trace &tr = g_trace;
+    const bool rec = tr.events && tr.count < tr.n_pairs;
+    hipEvent_t e0 = rec ? (hipEvent_t)tr.events[2 * tr.count] : nullptr;
+    hipEvent_t e1 = rec ? (hipEvent_t)tr.events[2 * tr.count + 1] : nullptr;
+    if (hipExtLaunchKernel(kernel, grid, block, args, 0, stream, e0, e1, 0) != hipSuccess)
         return fail(SNAPKV_EHIP, std::string("kernel launch failed: ") + hipGetErrorString(hipGetLastError()));
+    if (tr.events) {
+        if (rec && tr.count < 4096) tr.ids[tr.count] = id;
+        ++tr.count;
+    }
     return SNAPKV_OK;
+}
+
+int launch(int id, const void *kernel, dim3 grid, dim3 block, void *arg, hipStream_t stream) {
+    return launch_traced(id, kernel, grid, block, arg, stream);
 }
 
 int fill_u32(uint32_t *ptr, int64_t n, uint32_t v, hipStream_t stream) {
@@ -257,11 +282,13 @@ int fill_u32(uint32_t *ptr, int64_t n, uint32_t v, hipStream_t stream) {
     int64_t blocks = (n + 255) / 256;
     if (blocks > 1024) blocks = 1024;
     if (blocks < 1) blocks = 1;
-    return launch(fill_kernel(), dim3((unsigned)blocks), dim3(256), &fp, stream);
+    return launch(SNAPKV_K_FILL, fill_kernel(), dim3((unsigned)blocks), dim3(256), &fp, stream);
 }
 
-// Scores of every group: votes (into `votes`) and pooled votes (into `pooled`).
-int run_scores(const Plan &p, const void *q, const void *K, float *votes, float *pooled, char *ws,
+int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream);
+
+// Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
+int run_scores(const Plan &p, const void *q, const void *K, float *votes, float *pooled, bool pool, char *ws,
                hipStream_t stream) {
     DevInfo di;
     int st = device_info(&di);
@@ -300,19 +327,20 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         op.slab_keys = slab;
         op.spin_limit = kSpinLimit;
         op.rt = gr.rt;
-        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && di.coop && resident > 0 && gr.max_ns <= resident;
+        // The fused kernel's grid never exceeds what the device keeps resident, and no
+        // segment has more slabs than that grid, so every segment barrier completes.
+        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && gr.max_ns <= resident;
         const int n_seg = gr.rt.n * p.Hkv;
         if (fused) {
             st = fill_u32(err, 1 + (int64_t)n_seg, 0u, stream);  // error word and arrival counters
             if (st) return st;
             const int grid = gr.n_slabs < resident ? gr.n_slabs : resident;
-            void *args[] = {&op};
-            if (hipLaunchCooperativeKernel(kf, dim3(grid), dim3(cfg.threads()), args, 0, stream) != hipSuccess)
-                return fail(SNAPKV_EHIP, std::string("cooperative launch failed: ") + hipGetErrorString(hipGetLastError()));
+            st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);
+            if (st) return st;
         } else {
             st = fill_u32(err, 1, 0u, stream);
             if (st) return st;
-            st = launch(obs_kernel(p.dtype, p.d, p.M_pad, kStats), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, p.M_pad, kStats), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
             if (st) return st;
             MergeParams mp;
             memset(&mp, 0, sizeof mp);
@@ -324,12 +352,37 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
             mp.Hkv = p.Hkv;
             mp.c = op.c;
             mp.rt = gr.rt;
-            st = launch(merge_kernel(), dim3(n_seg), dim3(256), &mp, stream);
+            st = launch(SNAPKV_K_STATS_MERGE, merge_kernel(), dim3(n_seg), dim3(256), &mp, stream);
             if (st) return st;
-            st = launch(obs_kernel(p.dtype, p.d, p.M_pad, kVotes), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, p.M_pad, kVotes), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
             if (st) return st;
         }
-        if (gr.max_P > 0) {
+        if (gr.max_P > 0 && pool) {
+            st = run_pool(p, gr, votes, pooled, stream);
+            if (st) return st;
+        }
+    }
+    return SNAPKV_OK;
+}
+
+// Pooled votes of one group: in the select kernel's LDS pass when every segment fits
+// there, else with the pooling kernel.
+int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream) {
+    {
+        if (gr.max_P <= select_lds_positions()) {
+            SelectParams sp;
+            memset(&sp, 0, sizeof sp);
+            sp.votes = votes;
+            sp.pooled_out = pooled;
+            sp.sum_P = p.sum_P;
+            sp.sum_k = p.sum_k;
+            sp.w = p.w;
+            sp.Hkv = p.Hkv;
+            sp.half = p.K_pool / 2;
+            sp.rt = gr.rt;
+            return launch(SNAPKV_K_POOL, select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp, stream);
+        }
+        {
             PoolParams pp;
             memset(&pp, 0, sizeof pp);
             pp.votes = votes;
@@ -338,26 +391,36 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
             pp.w = p.w;
             pp.half = p.K_pool / 2;
             pp.rt = gr.rt;
-            st = launch(pool_kernel(), dim3((gr.max_P + 255) / 256, gr.rt.n, p.Hkv), dim3(256), &pp, stream);
-            if (st) return st;
+            return launch(SNAPKV_K_POOL, pool_kernel(), dim3((gr.max_P + 255) / 256, gr.rt.n, p.Hkv), dim3(256), &pp,
+                          stream);
         }
     }
-    return SNAPKV_OK;
 }
 
-int run_select(const Plan &p, const float *pooled, int32_t *idx, hipStream_t stream) {
-    if (p.sum_k == 0) return SNAPKV_OK;
+// Top-k of every group.  With `votes`, segments that fit in LDS are pooled there first
+// (pooled votes also written to `pooled` if it is not null); longer segments are pooled
+// by the pooling kernel into `pooled`, which must then be given.
+int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, hipStream_t stream) {
     for (const Group &gr : p.groups) {
+        const bool in_lds = gr.max_P <= select_lds_positions();
+        if (votes && !in_lds) {
+            int st = run_pool(p, gr, votes, pooled, stream);
+            if (st) return st;
+        }
+        if (p.cu_k[gr.rt.qi[gr.rt.n - 1] + 1] == p.cu_k[gr.rt.qi[0]] && !(votes && in_lds && pooled)) continue;
         SelectParams sp;
         memset(&sp, 0, sizeof sp);
+        sp.votes = (votes && in_lds) ? votes : nullptr;
         sp.pooled = pooled;
+        sp.pooled_out = (votes && in_lds) ? pooled : nullptr;
         sp.idx = idx;
         sp.sum_P = p.sum_P;
         sp.sum_k = p.sum_k;
         sp.w = p.w;
         sp.Hkv = p.Hkv;
+        sp.half = p.K_pool / 2;
         sp.rt = gr.rt;
-        int st = launch(select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp, stream);
+        int st = launch(SNAPKV_K_SELECT, select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp, stream);
         if (st) return st;
     }
     return SNAPKV_OK;
@@ -386,7 +449,7 @@ int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, 
         int64_t blocks = (gr.out_rows + rpb - 1) / rpb;
         if (blocks > 65535) blocks = 65535;
         if (blocks < 1) blocks = 1;
-        int st = launch(gather_kernel(), dim3((unsigned)blocks, p.Hkv), dim3(256), &gp, stream);
+        int st = launch(SNAPKV_K_GATHER, gather_kernel(), dim3((unsigned)blocks, p.Hkv), dim3(256), &gp, stream);
         if (st) return st;
     }
     return SNAPKV_OK;
@@ -439,7 +502,7 @@ int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, fl
     if (st) return st;
     char *w = (char *)ws;
     float *v = votes ? votes : (float *)(w + p.off_votes);
-    return finish(run_scores(p, q_obs, K, v, pooled, w, (hipStream_t)stream));
+    return finish(run_scores(p, q_obs, K, v, pooled, true, w, (hipStream_t)stream));
 }
 
 int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, void *ws, size_t ws_bytes,
@@ -453,7 +516,7 @@ int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, v
     DevInfo di;
     st = device_info(&di);
     if (st) return st;
-    return finish(run_select(p, pooled, idx, (hipStream_t)stream));
+    return finish(run_select(p, nullptr, (float *)pooled, idx, (hipStream_t)stream));
 }
 
 int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const int32_t *idx, void *K_out,
@@ -488,12 +551,46 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
     char *w = (char *)ws;
     hipStream_t s = (hipStream_t)stream;
     float *votes = (float *)(w + p.off_votes);
-    float *pl = pooled ? pooled : (float *)(w + p.off_pooled);
+    // pooled votes: the caller's buffer, or workspace when long segments need them in memory
+    float *pl = pooled ? pooled : (p.max_P > select_lds_positions() ? (float *)(w + p.off_pooled) : nullptr);
     int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
-    st = run_scores(p, q_obs, K, votes, pl, w, s);
-    if (!st) st = run_select(p, pl, ix, s);
+    st = run_scores(p, q_obs, K, votes, nullptr, false, w, s);
+    if (!st) st = run_select(p, votes, pl, ix, s);
     if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s);
     return finish(st);
+}
+
+int snapkv_trace_begin(void *const *events, int n_pairs) {
+    g_last_error.clear();
+    if (!events || n_pairs < 1) return fail(SNAPKV_EINVAL, "trace needs events and n_pairs >= 1");
+    g_trace.events = events;
+    g_trace.n_pairs = n_pairs;
+    g_trace.count = 0;
+    return SNAPKV_OK;
+}
+
+int snapkv_trace_end(int32_t *kernel_ids, int capacity) {
+    const int n = g_trace.count < g_trace.n_pairs ? g_trace.count : g_trace.n_pairs;
+    for (int i = 0; kernel_ids && i < n && i < capacity && i < 4096; ++i) kernel_ids[i] = g_trace.ids[i];
+    const int count = g_trace.count;
+    g_trace.events = nullptr;
+    g_trace.n_pairs = 0;
+    g_trace.count = 0;
+    return count;
+}
+
+const char *snapkv_kernel_name(int id) {
+    switch (id) {
+        case SNAPKV_K_FILL: return "fill_u32";
+        case SNAPKV_K_OBS_FUSED: return "obs_score_fused";
+        case SNAPKV_K_OBS_STATS: return "obs_score_stats";
+        case SNAPKV_K_STATS_MERGE: return "obs_stats_merge";
+        case SNAPKV_K_OBS_VOTES: return "obs_score_votes";
+        case SNAPKV_K_POOL: return "vote_pool";
+        case SNAPKV_K_SELECT: return "topk_select";
+        case SNAPKV_K_GATHER: return "kv_gather";
+        default: return "unknown";
+    }
 }
 
 const char *snapkv_strerror(int status) {

@@ -10,16 +10,19 @@
 //   * A work unit ("slab") is one (request, KV head) segment's run of SLAB consecutive
 //     keys.  Logits S = Q K^T are a dense contraction of depth d, computed with
 //     v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32).  A = window
-//     queries (held in VGPRs for the whole slab), B = keys streamed from HBM straight
-//     into the MFMA operand layout, 16-byte loads, two key tiles in flight per wave.
+//     queries (LDS, or VGPRs when several waves split the rows), B = keys streamed from
+//     HBM straight into the MFMA operand layout, 16-byte loads, PF key tiles in flight
+//     per wave.
 //   * The d-dimension of each lane's operand is permuted so that one load instruction
 //     covers 64 contiguous bytes of each of 16 key rows; A and B use the same
 //     permutation, so every dot product is unchanged.
 //   * kFused keeps the slab's logits in registers: per-row max and sum of exponentials
 //     over the slab are published, the slabs of a segment meet at a counter barrier
-//     (grid launched cooperatively, so all slabs of a segment are resident), each slab
+//     (the grid never exceeds what the device keeps resident and a segment never has
+//     more slabs than the grid, so every slab of a segment is running), each slab
 //     merges the segment's row stats and turns its resident logits into votes.  K is
-//     read from HBM once.
+//     read from HBM once.  Row stats and counters move through device-coherent (sc1)
+//     atomic loads and stores, so the barrier needs no L2 write-back or invalidate.
 //   * kStats / kVotes are the two-pass path for segments with more slabs than fit on
 //     the chip at once: first pass publishes stats, merge_kernel combines them, second
 //     pass recomputes the logits and writes votes.
@@ -161,45 +164,44 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             const char *kb = (const char *)p.K +
                              ((int64_t)sp.g * p.head_stride + p.rt.tok0[sp.r] * p.token_stride) * ESZ + grp * 16;
             const int64_t tstride = p.token_stride * ESZ;
+            // No branches in this loop: a tile past the request end loads its last row again
+            // (in bounds) and is masked below; a branch here would make the compiler drain
+            // every outstanding load before the next tile's loads issue.
             u32x4_t buf[PF][NQ];
 #pragma unroll
-            for (int f = 0; f < PF; ++f) {
-                if (f < CTW && kw0 + f * 16 < L) {
-                    int j = kw0 + f * 16 + n16;
-                    j = j < L ? j : L - 1;
-                    const char *a = kb + (int64_t)j * tstride;
+            for (int f = 0; f < PF && f < CTW; ++f) {
+                int j = kw0 + f * 16 + n16;
+                j = j < L ? j : L - 1;
+                const char *a = kb + (int64_t)j * tstride;
 #pragma unroll
-                    for (int qq = 0; qq < NQ; ++qq) buf[f][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
-                }
+                for (int qq = 0; qq < NQ; ++qq) buf[f][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
             }
 #pragma unroll
             for (int ct = 0; ct < CTW; ++ct) {
-                if (kw0 + ct * 16 < L) {
-                    u32x4_t cur[NQ];
+                u32x4_t cur[NQ];
 #pragma unroll
-                    for (int qq = 0; qq < NQ; ++qq) cur[qq] = buf[ct % PF][qq];
-                    if (ct + PF < CTW && kw0 + (ct + PF) * 16 < L) {
-                        int j = kw0 + (ct + PF) * 16 + n16;
-                        j = j < L ? j : L - 1;
-                        const char *a = kb + (int64_t)j * tstride;
+                for (int qq = 0; qq < NQ; ++qq) cur[qq] = buf[ct % PF][qq];
+                if (ct + PF < CTW) {  // resolved at compile time after unrolling
+                    int j = kw0 + (ct + PF) * 16 + n16;
+                    j = j < L ? j : L - 1;
+                    const char *a = kb + (int64_t)j * tstride;
+#pragma unroll
+                    for (int qq = 0; qq < NQ; ++qq)
+                        buf[ct % PF][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
+                }
+                if constexpr (QLDS) {
+                    // keep the compiler from merging the per-tile LDS reads into registers
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
                         for (int qq = 0; qq < NQ; ++qq)
-                            buf[ct % PF][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
-                    }
-                    if constexpr (QLDS) {
-                        // keep the compiler from merging the per-tile LDS reads into registers
-                        asm volatile("" ::: "memory");
+                            S[rt][ct] = Dot<T>::step(sh_q[rt * 16 + n16][4 * qq + grp], cur[qq], S[rt][ct]);
+                } else {
 #pragma unroll
-                        for (int rt = 0; rt < RTW; ++rt)
+                    for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-                            for (int qq = 0; qq < NQ; ++qq)
-                                S[rt][ct] = Dot<T>::step(sh_q[rt * 16 + n16][4 * qq + grp], cur[qq], S[rt][ct]);
-                    } else {
-#pragma unroll
-                        for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-                            for (int qq = 0; qq < NQ; ++qq) S[rt][ct] = Dot<T>::step(qf[rt][qq], cur[qq], S[rt][ct]);
-                    }
+                        for (int qq = 0; qq < NQ; ++qq) S[rt][ct] = Dot<T>::step(qf[rt][qq], cur[qq], S[rt][ct]);
                 }
             }
         }
@@ -299,7 +301,14 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                        if (row < p.M) p.partial[(int64_t)s * p.M_pad + row] = make_float2(mrow[rt][i], lrow[rt][i]);
+                        if (row < p.M) {
+                            // device-coherent store (bypasses the per-XCD L2): the barrier below
+                            // needs no cache write-back
+                            const float2 v = make_float2(mrow[rt][i], lrow[rt][i]);
+                            __hip_atomic_store((uint64_t *)&p.partial[(int64_t)s * p.M_pad + row],
+                                               __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                        }
                         sh_rowm[row] = mrow[rt][i];
                     }
             }
@@ -313,30 +322,35 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
         if constexpr (MODE == kFused) {
             // All slabs of the segment publish, then meet.  Every slab publishes before it
             // waits, and a segment never has more slabs than resident workgroups, so the
-            // wait ends; a poll limit turns a broken launch into an error bit instead of a hang.
-            __threadfence();
+            // wait ends; a poll limit turns a device that did not keep the grid resident
+            // (another process filling the CUs) into an error bit instead of a hang.
+            // Each wave's device-coherent stores complete (vmcnt 0) before the workgroup
+            // barrier, so the arrival below is ordered after every published row stat.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (tid == 0) {
-                atomicAdd(&p.counters[seg], 1u);
+                __hip_atomic_fetch_add(&p.counters[seg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 uint32_t spins = 0;
                 while (__hip_atomic_load(&p.counters[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                        (uint32_t)sp.ns) {
                     __builtin_amdgcn_s_sleep(2);
                     if (++spins > p.spin_limit) {
-                        atomicOr(p.err, 1u);
+                        __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
                 }
             }
             __syncthreads();
-            __threadfence();
+            asm volatile("" ::: "memory");
             // Merge the segment's row stats; factor for this slab's resident weights.
             constexpr int TPR = NT / MROWS;  // threads per row (power of two)
             const int row = tid / TPR, sub = tid - (tid / TPR) * TPR;
             float mm = neg_inf(), ll = 0.f;
             if (row < p.M) {
                 for (int s2 = sub; s2 < sp.ns; s2 += TPR) {
-                    const float2 pr = p.partial[(int64_t)(sp.seg_slab0 + s2) * p.M_pad + row];
+                    const uint64_t bits = __hip_atomic_load((uint64_t *)&p.partial[(int64_t)(sp.seg_slab0 + s2) * p.M_pad + row],
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    const float2 pr = __builtin_bit_cast(float2, bits);
                     merge_stats(mm, ll, pr.x, pr.y, c);
                 }
             }

@@ -79,14 +79,17 @@ struct PoolParams {
 const void *pool_kernel();
 
 struct SelectParams {
-    const float *pooled;
-    int32_t *idx;
+    const float *votes;         // votes to pool first (segments held in LDS), or null
+    const float *pooled;        // pooled votes to select from when votes is null
+    float *pooled_out;          // pooled votes written here when pooling here, or null
+    int32_t *idx;               // chosen positions, or null (pooling only)
     int64_t sum_P, sum_k;
-    int32_t w, Hkv;
+    int32_t w, Hkv, half;       // half = K_pool / 2
     ReqTable rt;
 };
 const void *select_kernel();
 int select_threads();
+int select_lds_positions();     // longest segment pooled and selected in LDS
 
 struct GatherParams {
     const void *K, *V;
