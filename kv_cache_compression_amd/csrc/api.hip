@@ -100,6 +100,9 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.head_stride < 0) return fail(SNAPKV_EINVAL, "kv_head_stride must be >= 0");
     if ((p.token_stride * p.esz) % 16 || (p.head_stride * p.esz) % 16)
         return fail(SNAPKV_EINVAL, "K/V strides must keep rows 16-byte aligned");
+    // a slab's keys are addressed with 32-bit offsets from the slab's first key
+    if ((double)p.token_stride * p.esz * p.cfg.slab_keys() >= 2147483648.0)
+        return fail(SNAPKV_EUNSUPPORTED, "kv_token_stride too large (one slab of keys must span < 2 GiB)");
 
     const int32_t *cu = pb->cu_seqlens_host;
     if (cu[0] != 0) return fail(SNAPKV_EINVAL, "cu_seqlens[0] must be 0");
@@ -171,11 +174,11 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     for (int r = 0; r < p.B; ++r)
         if (cu[r + 1] > 0x7fffffff - 1) return fail(SNAPKV_EUNSUPPORTED, "token count exceeds int32");
 
-    // workspace: [err | counters] [partial] [merged] [votes] [pooled] [idx]
+    // workspace: [err (one 256-byte line)] [counters, one line each] [partial] [merged] [votes] [pooled] [idx]
     size_t off = 0;
     p.off_err = off;
-    p.off_cnt = off + sizeof(uint32_t);
-    off = align_up(sizeof(uint32_t) * (1 + (size_t)p.max_group_segs));
+    p.off_cnt = kWsAlign;
+    off = align_up(p.off_cnt + sizeof(uint32_t) * kCounterStride * (size_t)p.max_group_segs);
     p.off_partial = off;
     off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_slabs * p.M_pad);
     p.off_merged = off;
@@ -332,7 +335,8 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && gr.max_ns <= resident;
         const int n_seg = gr.rt.n * p.Hkv;
         if (fused) {
-            st = fill_u32(err, 1 + (int64_t)n_seg, 0u, stream);  // error word and arrival counters
+            // error word and arrival counters (contiguous from the start of the workspace)
+            st = fill_u32(err, (int64_t)(p.off_cnt / sizeof(uint32_t)) + (int64_t)kCounterStride * n_seg, 0u, stream);
             if (st) return st;
             const int grid = gr.n_slabs < resident ? gr.n_slabs : resident;
             st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);

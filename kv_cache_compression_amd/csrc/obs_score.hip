@@ -78,6 +78,41 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Reductions inside a row of 16 lanes (DPP row rotations, no LDS round trip): every lane
+// of the row ends with the row's max / sum.
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0x128>(v));  // row_ror:8
+    v = fmaxf(v, dpp_mov<0x124>(v));  // row_ror:4
+    v = fmaxf(v, dpp_mov<0x122>(v));  // row_ror:2
+    v = fmaxf(v, dpp_mov<0x121>(v));  // row_ror:1
+    return v;
+}
+__device__ inline float row16_sum(float v) {
+    v += dpp_mov<0x128>(v);
+    v += dpp_mov<0x124>(v);
+    v += dpp_mov<0x122>(v);
+    v += dpp_mov<0x121>(v);
+    return v;
+}
+// Sum of lanes i, i^16, i^32, i^48 (the four row groups of an MFMA output column).
+__device__ inline float cross_row_sum4(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // lanes i and i^32
+    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const unsigned us = __float_as_uint(s);
+    const auto b = __builtin_amdgcn_permlane16_swap(us, us, false, false);  // then i and i^16
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Buffer descriptor word 3 for gfx9 untyped loads (32-bit data format), and the
+// non-temporal cache policy bit of the load.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kNonTemporal = 2;
+
 struct SlabPos {
     int r, g, sl, ns;
     int seg_slab0;  // first slab of the segment
@@ -135,7 +170,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     __shared__ float sh_l[WK][MROWS];
     __shared__ float sh_rowm[MROWS];
     __shared__ float sh_f[MROWS];
-    __shared__ float sh_v[WR][SLAB];
+    __shared__ float sh_v[WR > 1 ? WR : 1][WR > 1 ? SLAB : 1];
     __shared__ int sh_wrow[MROWS];  // window row (row % L_obs) of each query row, for the causal mask
 
     const int tid = threadIdx.x;
@@ -184,16 +219,24 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
         f32x4_t S[RTW][CTW];
         static_for<RTW>([&](auto rt) { static_for<CTW>([&](auto ct) { S[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f}; }); });
         if constexpr (STAGED) {
-            const char *kseg = (const char *)p.K + ((int64_t)sp.g * p.head_stride + p.rt.tok0[sp.r] * p.token_stride) * ESZ;
+            // Buffer loads from a descriptor based at the slab's first key and sized to the
+            // slab's keys inside the request: the lane offset is fixed for the whole slab, the
+            // tile offset is a scalar, and rows past the request end read as zero (masked below).
             const int64_t tstride = p.token_stride * ESZ;
+            const char *slab0 = (const char *)p.K +
+                                ((int64_t)sp.g * p.head_stride + (p.rt.tok0[sp.r] + key0) * p.token_stride) * ESZ;
+            const int nkeys = L - key0 < SLAB ? L - key0 : SLAB;
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)slab0, (short)0, (int)(nkeys * tstride), kBufferFlags);
             const int lrow = lane >> 4, lch = lane & 15;  // load layout: row 4i + lrow, chunk lch
+            const int lane_off = (wk * 16 + lrow) * (int)tstride + lch * 16;
             u32x4_t *stile = sh_k[wave];
             u32x4_t buf[PF][4];
             auto load_tile = [&](auto slot, int ct) {
                 static_for<4>([&](auto i) {
-                    int key = tile_key(ct) + 4 * i + lrow;
-                    key = key < L ? key : L - 1;
-                    buf[slot][i] = __builtin_nontemporal_load((const u32x4_t *)(kseg + (int64_t)key * tstride + lch * 16));
+                    const int soff = (ct * WK * 16 + 4 * i) * (int)tstride;  // wave-uniform
+                    buf[slot][i] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, soff, kNonTemporal));
                 });
             };
             static_for<(PF < CTW ? PF : CTW)>([&](auto f) { load_tile(f, f); });
@@ -279,11 +322,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 static_for<4>([&](auto i) {
                     float m = S[rt][0][i()];
                     static_for<CTW - 1>([&](auto ct) { m = fmaxf(m, S[rt][ct + 1][i()]); });
-                    m = fmaxf(m, __shfl_xor(m, 1, 16));
-                    m = fmaxf(m, __shfl_xor(m, 2, 16));
-                    m = fmaxf(m, __shfl_xor(m, 4, 16));
-                    m = fmaxf(m, __shfl_xor(m, 8, 16));
-                    mrow[rt][i] = m;
+                    mrow[rt][i] = row16_max(m);
                 });
             });
             if constexpr (WK > 1) {
@@ -312,11 +351,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                         S[rt][ct][i()] = e;
                         l += e;
                     });
-                    l += __shfl_xor(l, 1, 16);
-                    l += __shfl_xor(l, 2, 16);
-                    l += __shfl_xor(l, 4, 16);
-                    l += __shfl_xor(l, 8, 16);
-                    lrow[rt][i] = l;
+                    lrow[rt][i] = row16_sum(l);
                 });
             });
             if constexpr (WK > 1) {
@@ -367,11 +402,11 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (tid == 0) {
-                __hip_atomic_fetch_add(&p.counters[seg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&p.counters[seg * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 uint32_t spins = 0;
-                while (__hip_atomic_load(&p.counters[seg], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                while (__hip_atomic_load(&p.counters[seg * kCounterStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
                        (uint32_t)sp.ns) {
-                    __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_s_sleep(8);
                     if (++spins > p.spin_limit) {
                         __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
@@ -431,24 +466,31 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             static_for<RTW>([&](auto rt) {
                 static_for<4>([&](auto i) { f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp + i]; });
             });
+            float *vout = p.votes + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
             static_for<CTW>([&](auto ct) {
                 float v = 0.f;
                 static_for<RTW>([&](auto rt) {
                     static_for<4>([&](auto i) { v = fmaf(S[rt][ct][i()], f[rt][i], v); });
                 });
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                if (grp == 0) sh_v[wr][(ct * WK + wk) * 16 + n16] = v;
+                v = cross_row_sum4(v);
+                if constexpr (WR == 1) {
+                    // this wave holds every row: its 16 lanes of group 0 store the tile's votes
+                    const int j = tile_key(ct) + n16;
+                    if (grp == 0 && j < P) vout[j] = v;
+                } else {
+                    if (grp == 0) sh_v[wr][(ct * WK + wk) * 16 + n16] = v;
+                }
             });
-            __syncthreads();
-            float *vout = p.votes + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
-            for (int t = tid; t < SLAB; t += NT) {
-                const int j = key0 + t;
-                if (j < P) {
-                    float a = sh_v[0][t];
+            if constexpr (WR > 1) {
+                __syncthreads();
+                for (int t = tid; t < SLAB; t += NT) {
+                    const int j = key0 + t;
+                    if (j < P) {
+                        float a = sh_v[0][t];
 #pragma unroll
-                    for (int w2 = 1; w2 < WR; ++w2) a += sh_v[w2][t];
-                    vout[j] = a;
+                        for (int w2 = 1; w2 < WR; ++w2) a += sh_v[w2][t];
+                        vout[j] = a;
+                    }
                 }
             }
             __syncthreads();

@@ -9,6 +9,9 @@ namespace snapkv {
 // Requests handled by one group of launches.  Larger batches are cut into
 // groups; the per-request table travels as a kernel argument (no copies).
 constexpr int kMaxReq = 32;
+// Barrier counters sit one 256-byte line apart, so the polls of different segments do not
+// pile onto one memory channel while other workgroups still stream keys.
+constexpr int kCounterStride = 64;  // uint32 words
 
 struct ReqTable {
     int32_t n;                    // requests in this group
@@ -35,7 +38,7 @@ struct ObsParams {
     float *votes;               // [H_kv][sum_P]
     float2 *partial;            // [slabs][M_pad]: (max of raw logits, sum of exp2((s-max)*c))
     const float2 *merged;       // [segments][M_pad]: merged (max, sum) for kVotes
-    uint32_t *counters;         // [segments] arrival counters for kFused
+    uint32_t *counters;         // [segments * kCounterStride] arrival counters for kFused
     uint32_t *err;              // error word (bit 0: a barrier wait gave up)
     int64_t head_stride;        // elements
     int64_t token_stride;       // elements
