@@ -46,7 +46,27 @@ def parse():
     ap.add_argument("--two-pass", action="store_true", help="force the two-pass scoring path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 launches) and exit: the known-size "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """dst = src * 1 on float32 buffers of `mib` MiB: reads and writes exactly mib MiB per launch."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20) // 4
+    src = torch.rand(n, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    if not torch.equal(src, dst):
+        raise RuntimeError("copy calibration produced a wrong copy")
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
 
 
 class Hip:
@@ -103,6 +123,9 @@ def main():
               "A multi-GPU split would shard KV heads with no exchange; it is not built here." % (args.gpus, world),
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
