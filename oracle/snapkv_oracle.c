@@ -17,7 +17,7 @@
  *     times keys over sqrt(d_k), sum, max pooling with padding kernel//2 and
  *     stride 1, top-k, ascending sort of indices, per-head gather, concat).
  *
- * Readings where the page is silent or differs (each is listed in the design doc):
+ * Readings where the page is silent or differs:
  *   - softmax denominator: every key visible to the window row, i.e. the
  *     prefix plus the window up to and including the row's own position
  *     (causal inside the window).  The listing's prefix-only variant is
