@@ -108,11 +108,15 @@ typedef struct {
  *   ws_bytes          : workspace bytes that snapkv_scores, snapkv_select and
  *                       snapkv_compress need for this problem (device
  *                       independent; 0 is never returned).
- * Workspace contents: after a scoring call completes on its stream, the first
- * 4 bytes hold an error word: 0 = fine; bit 0 set = a per-segment barrier gave
- * up waiting (only possible if other work kept part of the scoring grid off
- * the GPU for about a second); the outputs of that call are then invalid and
- * SNAPKV_FLAG_TWO_PASS, which has no barrier, computes them.
+ * Workspace contract: zero-fill it once before its first use.  Every call
+ * leaves its barrier counters at zero again, so later calls (also under graph
+ * replay) need no clearing.  The first 4 bytes hold a sticky error word that
+ * only the caller clears: bit 0 = a per-segment barrier gave up waiting (only
+ * possible if other work kept part of the scoring grid off the GPU for about a
+ * second); bit 1 = a barrier counter was not zero when a call started (the
+ * workspace was not zero-filled, or was shared by calls running at the same
+ * time).  With either bit set the outputs of the calls since it was last clear
+ * may be invalid; SNAPKV_FLAG_TWO_PASS, which has no barrier, computes them.
  * Returns SNAPKV_OK or SNAPKV_EINVAL / SNAPKV_EUNSUPPORTED.
  */
 int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host, int64_t *cu_k_host,
@@ -123,7 +127,8 @@ int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host,
  *   q_obs, K : inputs as laid out above (dtype of the problem).
  *   votes    : out, float32 [H_kv][sum_P], or NULL to skip writing C.
  *   pooled   : out, float32 [H_kv][sum_P], max pooled votes.
- *   ws       : device workspace of at least snapkv_plan's ws_bytes, 256-byte aligned.
+ *   ws       : device workspace of at least snapkv_plan's ws_bytes, 256-byte
+ *              aligned, zero-filled before its first use (see snapkv_plan).
  */
 int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, float *votes, float *pooled,
                   void *ws, size_t ws_bytes, void *stream);
@@ -169,7 +174,7 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
  *                       returns count (>= 0).
  */
 typedef enum {
-    SNAPKV_K_FILL = 0,        /* zero the error word and barrier counters */
+    SNAPKV_K_RESERVED0 = 0,   /* not launched (ids stay stable) */
     SNAPKV_K_OBS_FUSED = 1,   /* obs_score, logits resident, one read of K */
     SNAPKV_K_OBS_STATS = 2,   /* obs_score two-pass: row stats */
     SNAPKV_K_STATS_MERGE = 3, /* obs_score two-pass: merge of row stats */

@@ -185,7 +185,7 @@ def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, vari
 
 
 def workspace(spec: Spec, device) -> torch.Tensor:
-    ws = torch.empty(spec.ws_bytes, dtype=torch.uint8, device=device)
+    ws = torch.zeros(spec.ws_bytes, dtype=torch.uint8, device=device)  # zero-filled once, as the library requires
     if ws.data_ptr() % 256:
         raise RuntimeError("torch returned a workspace that is not 256-byte aligned")
     return ws

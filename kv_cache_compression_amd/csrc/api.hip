@@ -280,14 +280,6 @@ int launch(int id, const void *kernel, dim3 grid, dim3 block, void *arg, hipStre
     return launch_traced(id, kernel, grid, block, arg, stream);
 }
 
-int fill_u32(uint32_t *ptr, int64_t n, uint32_t v, hipStream_t stream) {
-    FillParams fp{ptr, n, v};
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 1024) blocks = 1024;
-    if (blocks < 1) blocks = 1;
-    return launch(SNAPKV_K_FILL, fill_kernel(), dim3((unsigned)blocks), dim3(256), &fp, stream);
-}
-
 int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream);
 
 // Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
@@ -335,15 +327,10 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && gr.max_ns <= resident;
         const int n_seg = gr.rt.n * p.Hkv;
         if (fused) {
-            // error word and arrival counters (contiguous from the start of the workspace)
-            st = fill_u32(err, (int64_t)(p.off_cnt / sizeof(uint32_t)) + (int64_t)kCounterStride * n_seg, 0u, stream);
-            if (st) return st;
             const int grid = gr.n_slabs < resident ? gr.n_slabs : resident;
             st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);
             if (st) return st;
         } else {
-            st = fill_u32(err, 1, 0u, stream);
-            if (st) return st;
             st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, p.M_pad, kStats), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
             if (st) return st;
             MergeParams mp;
@@ -369,11 +356,17 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
     return SNAPKV_OK;
 }
 
-// Pooled votes of one group: in the select kernel's LDS pass when every segment fits
-// there, else with the pooling kernel.
+// Whether the select kernel pools the votes itself: every segment of the group fits its
+// resident path and the pool window is narrow enough.
+bool select_pools(const Plan &p, int max_P) {
+    return max_P <= select_lds_positions() && p.K_pool / 2 <= select_max_half(max_P);
+}
+
+// Pooled votes of one group: in the select kernel when it can pool (see select_pools),
+// else with the pooling kernel.
 int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream) {
     {
-        if (gr.max_P <= select_lds_positions()) {
+        if (select_pools(p, gr.max_P)) {
             SelectParams sp;
             memset(&sp, 0, sizeof sp);
             sp.votes = votes;
@@ -406,7 +399,7 @@ int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, 
 // by the pooling kernel into `pooled`, which must then be given.
 int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, hipStream_t stream) {
     for (const Group &gr : p.groups) {
-        const bool in_lds = gr.max_P <= select_lds_positions();
+        const bool in_lds = select_pools(p, gr.max_P);
         if (votes && !in_lds) {
             int st = run_pool(p, gr, votes, pooled, stream);
             if (st) return st;
@@ -449,8 +442,8 @@ int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, 
         gp.w = p.w;
         gp.Hkv = p.Hkv;
         gp.rt = gr.rt;
-        const int rpb = 256 / (p.row_bytes / 16);
-        int64_t blocks = (gr.out_rows + rpb - 1) / rpb;
+        const int tile = 256 / (p.row_bytes / 16) * gather_rows_per_thread();
+        int64_t blocks = (gr.out_rows + tile - 1) / tile;
         if (blocks > 65535) blocks = 65535;
         if (blocks < 1) blocks = 1;
         int st = launch(SNAPKV_K_GATHER, gather_kernel(), dim3((unsigned)blocks, p.Hkv), dim3(256), &gp, stream);
@@ -556,7 +549,7 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
     hipStream_t s = (hipStream_t)stream;
     float *votes = (float *)(w + p.off_votes);
     // pooled votes: the caller's buffer, or workspace when long segments need them in memory
-    float *pl = pooled ? pooled : (p.max_P > select_lds_positions() ? (float *)(w + p.off_pooled) : nullptr);
+    float *pl = pooled ? pooled : (!select_pools(p, p.max_P) ? (float *)(w + p.off_pooled) : nullptr);
     int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
     st = run_scores(p, q_obs, K, votes, nullptr, false, w, s);
     if (!st) st = run_select(p, votes, pl, ix, s);
@@ -585,7 +578,7 @@ int snapkv_trace_end(int32_t *kernel_ids, int capacity) {
 
 const char *snapkv_kernel_name(int id) {
     switch (id) {
-        case SNAPKV_K_FILL: return "fill_u32";
+        case SNAPKV_K_RESERVED0: return "reserved";
         case SNAPKV_K_OBS_FUSED: return "obs_score_fused";
         case SNAPKV_K_OBS_STATS: return "obs_score_stats";
         case SNAPKV_K_STATS_MERGE: return "obs_stats_merge";

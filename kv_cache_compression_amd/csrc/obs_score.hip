@@ -68,16 +68,6 @@ struct Dot<float> {
     }
 };
 
-// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so register arrays
-// are only ever indexed by constants (no reliance on the unroller).
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
-    }
-}
-
 // Reductions inside a row of 16 lanes (DPP row rotations, no LDS round trip): every lane
 // of the row ends with the row's max / sum.
 template <int CTRL>
@@ -399,18 +389,28 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             // (another process filling the CUs) into an error bit instead of a hang.
             // Each wave's device-coherent stores complete (vmcnt 0) before the workgroup
             // barrier, so the arrival below is ordered after every published row stat.
+            // The segment's two counters (arrivals, departures) start at zero; the last
+            // workgroup to depart sets both back to zero, so the next launch finds them
+            // zero without a clearing pass.  An arrival that finds the count already at
+            // the segment's size means the workspace was not zero-filled (error bit 1).
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (tid == 0) {
-                __hip_atomic_fetch_add(&p.counters[seg * kCounterStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                uint32_t *arrived = &p.counters[seg * kCounterStride];
+                const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (before >= (uint32_t)sp.ns) __hip_atomic_fetch_or(p.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 uint32_t spins = 0;
-                while (__hip_atomic_load(&p.counters[seg * kCounterStride], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-                       (uint32_t)sp.ns) {
+                while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)sp.ns) {
                     __builtin_amdgcn_s_sleep(8);
                     if (++spins > p.spin_limit) {
                         __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         break;
                     }
+                }
+                const uint32_t left = __hip_atomic_fetch_add(arrived + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (left == (uint32_t)sp.ns - 1) {
+                    __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(arrived + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             __syncthreads();

@@ -4,7 +4,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace snapkv {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1, so register arrays
+// are only ever indexed by constants (no reliance on the unroller).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
 
 // Requests handled by one group of launches.  Larger batches are cut into
 // groups; the per-request table travels as a kernel argument (no copies).
@@ -38,8 +50,8 @@ struct ObsParams {
     float *votes;               // [H_kv][sum_P]
     float2 *partial;            // [slabs][M_pad]: (max of raw logits, sum of exp2((s-max)*c))
     const float2 *merged;       // [segments][M_pad]: merged (max, sum) for kVotes
-    uint32_t *counters;         // [segments * kCounterStride] arrival counters for kFused
-    uint32_t *err;              // error word (bit 0: a barrier wait gave up)
+    uint32_t *counters;         // [segments * kCounterStride]: arrivals, departures (kFused)
+    uint32_t *err;              // error word (bit 0: a barrier wait gave up; bit 1: counters not zero)
     int64_t head_stride;        // elements
     int64_t token_stride;       // elements
     int64_t sum_P;
@@ -92,7 +104,8 @@ struct SelectParams {
 };
 const void *select_kernel();
 int select_threads();
-int select_lds_positions();     // longest segment pooled and selected in LDS
+int select_lds_positions();     // longest segment selected from LDS / registers
+int select_max_half(int max_P); // widest pool half-width (K_pool / 2) the select kernel pools itself
 
 struct GatherParams {
     const void *K, *V;
@@ -104,12 +117,7 @@ struct GatherParams {
     ReqTable rt;
 };
 const void *gather_kernel();
+int gather_rows_per_thread();
 
-struct FillParams {
-    uint32_t *p;
-    int64_t n;
-    uint32_t v;
-};
-const void *fill_kernel();
 
 }  // namespace snapkv

@@ -96,6 +96,10 @@ SMALL = [
     ("w1_d64", [300], 2, 2, 64, "bf16", 1, 7, 0.05, None, 0),
     ("pool1_topk_exact", [2000], 2, 2, 128, "bf16", 32, 1, 0.05, None, 8),
     ("varlen_gqa", [33, 2049, 700, 64, 4500], 8, 2, 128, "bf16", 32, 7, 0.05, None, 8),
+    ("pool31_half15", [3000], 4, 2, 64, "bf16", 16, 31, 0.05, None, 8),
+    ("pool17_run32", [20000], 2, 1, 64, "bf16", 16, 17, 0.05, None, 8),
+    ("pool33_run32", [20000], 2, 1, 64, "bf16", 16, 33, 0.05, None, 8),
+    ("pool41_pool_kernel", [2600, 900], 4, 2, 64, "bf16", 16, 41, 0.05, None, 8),
 ]
 
 
@@ -106,6 +110,47 @@ def test_small_shapes(case):
                       n_plant=n_plant, name=name)
     x, _ = run_and_check(wl)
     run_and_check(wl, two_pass=True, inputs=x)
+
+
+# Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
+# positions per thread of 1024) and past the 32768 positions it holds on chip.
+SELECT_P = [1, 2, 3, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 70001]
+
+
+@pytest.mark.parametrize("levels", [0, 3, 50])
+def test_select_exact_on_crafted_votes(levels):
+    """snapkv_select on given non-negative values equals the oracle's select exactly: heavy
+    ties (few distinct levels), exact zeros and negative zeros (which order as +0)."""
+    snap = _snap()
+    w = 4
+    lengths = [p + w for p in SELECT_P]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, Hkv, d = int(cu[-1]), 2, 64
+    q = torch.zeros((len(lengths), 2, w, d), dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros((Hkv, T, d), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(1234 + levels)
+    sum_P = sum(SELECT_P)
+    if levels == 0:
+        vals = rng.random((Hkv, sum_P)).astype(np.float32) * np.float32(1e-3)
+    else:
+        vals = (rng.integers(0, levels, (Hkv, sum_P)) / levels).astype(np.float32)
+    vals[:, rng.integers(0, sum_P, 100)] = np.float32(-0.0)
+    vals[:, rng.integers(0, sum_P, 100)] = np.float32(0.0)
+    pooled = torch.from_numpy(vals).cuda()
+    for kw in (dict(ratio=0.37), dict(budget=1), dict(budget=4097), dict(ratio=1.0)):
+        _say("select levels=%d %s" % (levels, kw))
+        spec = snap.make_spec(q, K, cu, w, 7, kw.get("ratio"), kw.get("budget"))
+        idx = snap.select(pooled, q, K, cu, obs_window=w, pool_kernel=7, **kw)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        pfx = np.concatenate([[0], np.cumsum(SELECT_P)])
+        for r, P in enumerate(SELECT_P):
+            k = int(spec.k[r])
+            for g in range(Hkv):
+                seg = vals[g, pfx[r]:pfx[r + 1]].astype(np.float64) + 0.0  # -0 -> +0
+                got = idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])]
+                np.testing.assert_array_equal(got.astype(np.int64), oracle.select(seg, k).astype(np.int64),
+                                              err_msg="P=%d k=%d g=%d %s" % (P, k, g, kw))
 
 
 def test_prefix_only_variant():
@@ -166,6 +211,27 @@ def test_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a["idx"], b["idx"]) and torch.equal(a["pooled"], b["pooled"])
     assert torch.equal(a["K_out"], b["K_out"]) and torch.equal(a["V_out"], b["V_out"])
+
+
+def test_workspace_counters_left_zero():
+    """The fused path's barrier counters return to zero after every call, so one
+    zero-filled workspace serves any number of calls; the error word stays clear."""
+    snap = _snap()
+    wl = synth.custom([3000, 1800], 8, 2, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8, name="ws_reuse")
+    x = synth.make_inputs(wl)
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    spec = snap.make_spec(q, K, x["cu_seqlens"], 32, 7, 0.05, None)
+    ws = snap.workspace(spec, K.device)
+    first = None
+    for it in range(3):
+        res = snap.compress(q, K, V, x["cu_seqlens"], obs_window=32, pool_kernel=7, ratio=0.05, ws=ws)
+        torch.cuda.synchronize()
+        # error line (256 B) and one 256-B counter line per (request, KV head) segment
+        head = ws[:256 * (1 + len(wl.lengths) * wl.num_kv_heads)].cpu().numpy()
+        assert not head.any(), "call %d left a nonzero error word or barrier counter" % it
+        if first is None:
+            first = res["idx"].clone()
+        assert torch.equal(first, res["idx"])
 
 
 def test_unsupported_rows_raise():
