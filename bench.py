@@ -226,6 +226,29 @@ def main():
             launch, graphs = "eager", []
             torch.cuda.synchronize()
 
+    # The timed graph holds all K steps back to back (step i on input set i mod n_sets), so
+    # the timed region is one graph launch; replaying one single-step graph per step adds the
+    # host's graph-launch gap to every step, reported beside it.
+    single_ms_per_step = None
+    if launch == "graph":
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            for i in range(args.steps):
+                graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        single_ms_per_step = (time.perf_counter() - s0) * 1e3 / args.steps
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all, stream=stream):
+            for i in range(args.steps):
+                enqueue(sets[i % n_sets])
+        for _ in range(max(1, -(-args.warmup // args.steps))):
+            g_all.replay()
+        torch.cuda.synchronize()
+
     # ---- timed region ---------------------------------------------------------------
     # Eager steps carry the kernel trace (events on the launch stream around every kernel).
     # Graph replays carry none (events inside a captured graph cannot be read back), so in
@@ -236,10 +259,10 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
-        for i in range(args.steps):
-            if launch == "graph":
-                graphs[i % n_sets].replay()
-            else:
+        if launch == "graph":
+            g_all.replay()
+        else:
+            for i in range(args.steps):
                 step_ids.append(traced(sets[i % n_sets], step_events[i]))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -325,6 +348,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "eager_traced_ms_per_step": round(eager_ms_per_step, 5) if eager_ms_per_step else None,
+        "single_step_graphs_ms_per_step": round(single_ms_per_step, 5) if single_ms_per_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -333,7 +357,8 @@ def main():
         "config": {"workload": wl.name, "num_q_heads": wl.num_q_heads, "num_kv_heads": Hkv, "head_dim": d,
                    "batch": wl.batch, "L_prompt": list(wl.lengths) if wl.batch > 1 else wl.lengths[0],
                    "L_obs": wl.obs_window, "K_pool": wl.pool_kernel, "p": wl.ratio, "budget": wl.budget,
-                   "layers_per_step": layers_per_step, "input_sets": n_sets, "launch": launch,
+                   "layers_per_step": layers_per_step, "input_sets": n_sets,
+                   "launch": "one graph of all timed steps" if launch == "graph" else launch,
                    "kernel_timing": "traced eager steps" + (" after the graph replays" if launch == "graph" else ""),
                    "scoring": "two_pass" if args.two_pass else "fused"},
         "roofline": {"kernel": obs_name, "bound": "hbm",

@@ -399,8 +399,9 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 uint32_t *arrived = &p.counters[seg * kCounterStride];
                 const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (before >= (uint32_t)sp.ns) __hip_atomic_fetch_or(p.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                uint32_t spins = 0;
-                while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)sp.ns) {
+                uint32_t spins = 0;  // the last arrival knows every slab has published
+                while (before + 1 < (uint32_t)sp.ns &&
+                       __hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)sp.ns) {
                     __builtin_amdgcn_s_sleep(8);
                     if (++spins > p.spin_limit) {
                         __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
