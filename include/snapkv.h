@@ -68,7 +68,7 @@ typedef enum {
     SNAPKV_OK = 0,
     SNAPKV_EINVAL = -1,       /* an argument is invalid (message: snapkv_last_error) */
     SNAPKV_EWORKSPACE = -2,   /* workspace missing, misaligned or smaller than snapkv_plan asks */
-    SNAPKV_EUNSUPPORTED = -3, /* valid but not supported: head_dim, G*L_obs > 256, device */
+    SNAPKV_EUNSUPPORTED = -3, /* valid but not supported: head_dim, G*L_obs > 1024, device */
     SNAPKV_EHIP = -4          /* the HIP runtime reported an error */
 } snapkv_status;
 
@@ -181,7 +181,8 @@ typedef enum {
     SNAPKV_K_OBS_VOTES = 4,   /* obs_score two-pass: votes */
     SNAPKV_K_POOL = 5,        /* vote_pool */
     SNAPKV_K_SELECT = 6,      /* topk_select */
-    SNAPKV_K_GATHER = 7       /* kv_gather */
+    SNAPKV_K_GATHER = 7,      /* kv_gather */
+    SNAPKV_K_SUM_CHUNKS = 8   /* sum of the votes of the row chunks (G * L_obs > 32) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -42,7 +42,7 @@ struct Group {
 struct Plan {
     int B, Hq, Hkv, d, w, K_pool, mode, dtype, variant;
     uint32_t flags;
-    int G, M, M_pad, esz, row_bytes;
+    int G, M, M_pad, n_chunks, esz, row_bytes;
     double ratio;
     int64_t budget, head_stride, token_stride;
     std::vector<int64_t> L, P, k, cu_pfx, cu_k, cu_out;
@@ -52,7 +52,7 @@ struct Plan {
     int max_group_slabs, max_group_segs;
     int64_t max_P;
     // workspace layout (bytes)
-    size_t off_err, off_cnt, off_partial, off_merged, off_votes, off_pooled, off_idx, ws_bytes;
+    size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx, ws_bytes;
 };
 
 int make_plan(const snapkv_problem *pb, Plan *pl) {
@@ -90,10 +90,11 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.d != 64 && p.d != 128) return fail(SNAPKV_EUNSUPPORTED, "head_dim must be 64 or 128");
     p.G = p.Hq / p.Hkv;
     const int64_t M = (int64_t)p.G * p.w;
-    if (M > 256) return fail(SNAPKV_EUNSUPPORTED, "G * obs_window must be <= 256");
+    if (M > kMaxRows) return fail(SNAPKV_EUNSUPPORTED, "G * obs_window must be <= " + std::to_string(kMaxRows));
     p.M = (int)M;
-    p.M_pad = (p.M + 15) / 16 * 16;
-    if (!obs_config(p.dtype, p.d, p.M_pad, &p.cfg)) return fail(SNAPKV_EUNSUPPORTED, "no kernel for this shape");
+    p.M_pad = kChunkRows;
+    p.n_chunks = (p.M + kChunkRows - 1) / kChunkRows;
+    if (!obs_config(p.dtype, p.d, &p.cfg)) return fail(SNAPKV_EUNSUPPORTED, "no kernel for this shape");
     p.esz = p.dtype == SNAPKV_F32 ? 4 : 2;
     p.row_bytes = p.d * p.esz;
     if (p.token_stride < p.d) return fail(SNAPKV_EINVAL, "kv_token_stride must be >= head_dim");
@@ -163,7 +164,7 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
             if (ns > gr.max_ns) gr.max_ns = (int)ns;
             if (p.P[r] > gr.max_P) gr.max_P = (int)p.P[r];
         }
-        if (slabs > (1 << 30)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
+        if (slabs * p.n_chunks > (1 << 30)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
         gr.rt.slab0[n] = (int32_t)slabs;
         gr.n_slabs = (int)slabs;
         gr.out_rows = p.cu_out[r0 + n] - p.cu_out[r0];
@@ -174,15 +175,19 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     for (int r = 0; r < p.B; ++r)
         if (cu[r + 1] > 0x7fffffff - 1) return fail(SNAPKV_EUNSUPPORTED, "token count exceeds int32");
 
-    // workspace: [err (one 256-byte line)] [counters, one line each] [partial] [merged] [votes] [pooled] [idx]
+    // workspace: [err (one 256-byte line)] [counters, one line per (segment, chunk)] [partial]
+    // [merged] [votes planes, when rows come in several chunks] [votes] [pooled] [idx]
+    const size_t C = (size_t)p.n_chunks;
     size_t off = 0;
     p.off_err = off;
     p.off_cnt = kWsAlign;
-    off = align_up(p.off_cnt + sizeof(uint32_t) * kCounterStride * (size_t)p.max_group_segs);
+    off = align_up(p.off_cnt + sizeof(uint32_t) * kCounterStride * (size_t)p.max_group_segs * C);
     p.off_partial = off;
-    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_slabs * p.M_pad);
+    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_slabs * C * p.M_pad);
     p.off_merged = off;
-    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_segs * p.M_pad);
+    off = align_up(off + sizeof(float) * 2 * (size_t)p.max_group_segs * C * p.M_pad);
+    p.off_planes = off;
+    if (C > 1) off = align_up(off + sizeof(float) * C * (size_t)p.Hkv * (size_t)p.sum_P);
     p.off_votes = off;
     off = align_up(off + sizeof(float) * (size_t)p.Hkv * (size_t)p.sum_P);
     p.off_pooled = off;
@@ -283,6 +288,25 @@ int launch(int id, const void *kernel, dim3 grid, dim3 block, void *arg, hipStre
 int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream);
 
 // Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
+// Whether a fused launch over the group runs without waits that span grid iterations:
+// work item v (a (slab, row chunk) pair) runs in iteration v / grid, and each segment's
+// items must lie in one iteration.  (A segment spanning two iterations still completes,
+// since no segment has more items than the grid, but its barrier then waits for the next
+// iteration's workgroups, which serialises the iterations.)
+static bool fused_fits(const Plan &p, const Group &gr, int grid) {
+    const int C = p.n_chunks;
+    for (int i = 0; i < gr.rt.n; ++i) {
+        const int ns = (gr.rt.L[i] + p.cfg.slab_keys() - 1) / p.cfg.slab_keys();
+        for (int g = 0; g < p.Hkv; ++g) {
+            const int64_t v0 = ((int64_t)gr.rt.slab0[i] + (int64_t)g * ns) * C;
+            const int64_t v1 = v0 + (int64_t)ns * C;  // exclusive
+            if (ns > 0 && v0 / grid != (v1 - 1) / grid) return false;
+        }
+    }
+    return true;
+}
+
+// Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
 int run_scores(const Plan &p, const void *q, const void *K, float *votes, float *pooled, bool pool, char *ws,
                hipStream_t stream) {
     DevInfo di;
@@ -290,11 +314,14 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
     if (st) return st;
     const ObsConfig &cfg = p.cfg;
     const int slab = cfg.slab_keys();
+    const int C = p.n_chunks;
+    const bool keep = C > 1;  // row chunks of a slab re-read it: keep it cached
     uint32_t *err = (uint32_t *)(ws + p.off_err);
     uint32_t *counters = (uint32_t *)(ws + p.off_cnt);
     float2 *partial = (float2 *)(ws + p.off_partial);
     float2 *merged = (float2 *)(ws + p.off_merged);
-    const void *kf = obs_kernel(p.dtype, p.d, p.M_pad, kFused);
+    float *planes = C > 1 ? (float *)(ws + p.off_planes) : votes;
+    const void *kf = obs_kernel(p.dtype, p.d, kFused, keep);
     const int occ = occupancy(kf, cfg.threads());
     const int resident = occ * di.cus;
     for (const Group &gr : p.groups) {
@@ -302,7 +329,7 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         memset(&op, 0, sizeof op);
         op.q = q;
         op.K = K;
-        op.votes = votes;
+        op.votes = planes;
         op.partial = partial;
         op.merged = merged;
         op.counters = counters;
@@ -321,17 +348,22 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         op.n_slabs = gr.n_slabs;
         op.slab_keys = slab;
         op.spin_limit = kSpinLimit;
+        op.n_chunks = C;
+        op.vplane = (int64_t)p.Hkv * p.sum_P;
         op.rt = gr.rt;
+        const int64_t items = (int64_t)gr.n_slabs * C;
+        const int grid = items < resident ? (int)items : resident;
         // The fused kernel's grid never exceeds what the device keeps resident, and no
-        // segment has more slabs than that grid, so every segment barrier completes.
-        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && gr.max_ns <= resident;
+        // segment has more work items than that grid, so every segment barrier completes.
+        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && (int64_t)gr.max_ns * C <= resident &&
+                           fused_fits(p, gr, grid);
         const int n_seg = gr.rt.n * p.Hkv;
         if (fused) {
-            const int grid = gr.n_slabs < resident ? gr.n_slabs : resident;
             st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);
             if (st) return st;
         } else {
-            st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, p.M_pad, kStats), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, kStats, keep), dim3((unsigned)items),
+                        dim3(cfg.threads()), &op, stream);
             if (st) return st;
             MergeParams mp;
             memset(&mp, 0, sizeof mp);
@@ -341,11 +373,28 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
             mp.M_pad = p.M_pad;
             mp.slab_keys = slab;
             mp.Hkv = p.Hkv;
+            mp.n_chunks = C;
             mp.c = op.c;
             mp.rt = gr.rt;
-            st = launch(SNAPKV_K_STATS_MERGE, merge_kernel(), dim3(n_seg), dim3(256), &mp, stream);
+            st = launch(SNAPKV_K_STATS_MERGE, merge_kernel(), dim3(n_seg * C, (p.M_pad + 3) / 4), dim3(256), &mp,
+                        stream);
             if (st) return st;
-            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, p.M_pad, kVotes), dim3(gr.n_slabs), dim3(cfg.threads()), &op, stream);
+            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, kVotes, keep), dim3((unsigned)items),
+                        dim3(cfg.threads()), &op, stream);
+            if (st) return st;
+        }
+        if (C > 1 && gr.max_P > 0) {
+            SumParams sp;
+            memset(&sp, 0, sizeof sp);
+            sp.planes = planes;
+            sp.votes = votes;
+            sp.sum_P = p.sum_P;
+            sp.vplane = op.vplane;
+            sp.col0 = gr.rt.pfx0[0];
+            sp.col1 = gr.rt.pfx0[gr.rt.n - 1] + (gr.rt.L[gr.rt.n - 1] - p.w);
+            sp.n_chunks = C;
+            st = launch(SNAPKV_K_SUM_CHUNKS, sum_kernel(), dim3((unsigned)((sp.col1 - sp.col0 + 255) / 256), p.Hkv),
+                        dim3(256), &sp, stream);
             if (st) return st;
         }
         if (gr.max_P > 0 && pool) {
@@ -586,6 +635,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_POOL: return "vote_pool";
         case SNAPKV_K_SELECT: return "topk_select";
         case SNAPKV_K_GATHER: return "kv_gather";
+        case SNAPKV_K_SUM_CHUNKS: return "sum_chunks";
         default: return "unknown";
     }
 }

@@ -123,6 +123,14 @@ __device__ inline SlabPos decode_slab(const ReqTable &rt, int s, int slab_keys) 
 
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
+// Key loads: non-temporal when every key is read once, cached when the row chunks of a
+// slab read it again.
+template <bool KEEP>
+__device__ inline u32x4_t load_key(const u32x4_t *a) {
+    if constexpr (KEEP) return *a;
+    else return __builtin_nontemporal_load(a);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // (m, l) pairs: l is a sum of exp2((s - m) * c).  Merge two of them.
@@ -139,7 +147,7 @@ __device__ inline void merge_stats(float &m, float &l, float m2, float l2, float
 // (p%16) ^ (p/16).  A load instruction's lane l carries row 4i + l/16, chunk l%16 (four
 // whole rows); the MFMA read of (row n, chunk c) by the 16 lanes of a lane group hits
 // slots 16n + (c ^ n): 16 distinct bank groups.
-template <typename T, int D, int WR, int WK, int RTW, int CTW, int MODE, bool STAGED = false>
+template <typename T, int D, int WR, int WK, int RTW, int CTW, int MODE, bool STAGED = false, bool KEEP = false>
 __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams p) {
     constexpr int NT = 64 * WR * WK;
     constexpr int ESZ = (int)sizeof(T);
@@ -161,37 +169,46 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     __shared__ float sh_rowm[MROWS];
     __shared__ float sh_f[MROWS];
     __shared__ float sh_v[WR > 1 ? WR : 1][WR > 1 ? SLAB : 1];
-    __shared__ int sh_wrow[MROWS];  // window row (row % L_obs) of each query row, for the causal mask
+    __shared__ int sh_wrow[kMaxRows];  // window row (row % L_obs) of each query row, for the causal mask
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wr = wave / WK, wk = wave - (wave / WK) * WK;
     const int n16 = lane & 15, grp = lane >> 4;
     const float c = p.c;
-    for (int r = tid; r < MROWS; r += NT) sh_wrow[r] = r % p.w;
+    for (int r = tid; r < kMaxRows; r += NT) sh_wrow[r] = r % p.w;
     __syncthreads();
 
-    for (int s = blockIdx.x; s < p.n_slabs; s += gridDim.x) {
+    // Work items are (slab, row chunk) pairs, chunk fastest.  With a grid that is a multiple
+    // of 8, consecutive items go to workgroups b, b+8, b+16, ... which the dispatcher places
+    // on one XCD, so the chunks of a slab read it from that XCD's L2.
+    const int C = p.n_chunks;
+    const int nb = gridDim.x;
+    const int b0 = (nb & 7) ? (int)blockIdx.x : ((int)blockIdx.x & 7) * (nb >> 3) + ((int)blockIdx.x >> 3);
+    for (int v = b0; v < p.n_slabs * C; v += nb) {
+        const int s = v / C, chunk = v - (v / C) * C;
         const SlabPos sp = decode_slab(p.rt, s, SLAB);
+        const int cbase = chunk * MROWS;                          // first query row of the chunk
+        const int Mc = p.M - cbase < MROWS ? p.M - cbase : MROWS;  // rows in this chunk
         const int L = p.rt.L[sp.r];
         const int P = L - p.w;
         const int key0 = sp.sl * SLAB;
         // tile ct of this wave holds keys key0 + (ct*WK + wk)*16 .. +15: at each step the
         // workgroup's waves read adjacent tiles
         auto tile_key = [&](int ct) { return key0 + (ct * WK + wk) * 16; };
-        const int seg = sp.r * p.Hkv + sp.g;
+        const int seg = (sp.r * p.Hkv + sp.g) * C + chunk;  // (segment, chunk) for stats and counters
 
         // Window queries of the group: rows r*G*L_obs .. of q_obs, zero beyond M.  With one
         // row wave and direct key loads (QLDS) they sit in LDS and are re-read per key tile,
         // which frees the VGPRs the resident logits need; otherwise each wave keeps its
         // rows in VGPRs.
         const char *qb = (const char *)p.q +
-                         ((int64_t)p.rt.qi[sp.r] * p.Hq + (int64_t)sp.g * p.G) * (int64_t)p.w * ROWB;
+                         (((int64_t)p.rt.qi[sp.r] * p.Hq + (int64_t)sp.g * p.G) * (int64_t)p.w + cbase) * ROWB;
         u32x4_t qf[QLDS ? 1 : RTW][NQ];
         if constexpr (QLDS) {
             for (int e = tid; e < MROWS * NCH; e += NT) {
                 const int row = e / NCH, ch = e - (e / NCH) * NCH;
-                sh_q[row][ch] = row < p.M ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + ch * 16)
+                sh_q[row][ch] = row < Mc ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + ch * 16)
                                           : u32x4_t{0u, 0u, 0u, 0u};
             }
             __syncthreads();
@@ -199,7 +216,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             static_for<RTW>([&](auto rt) {
                 const int row = (wr * RTW + rt) * 16 + n16;
                 static_for<NQ>([&](auto qq) {
-                    qf[rt][qq] = row < p.M ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + (4 * qq + grp) * 16)
+                    qf[rt][qq] = row < Mc ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + (4 * qq + grp) * 16)
                                            : u32x4_t{0u, 0u, 0u, 0u};
                 });
             });
@@ -226,7 +243,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 static_for<4>([&](auto i) {
                     const int soff = (ct * WK * 16 + 4 * i) * (int)tstride;  // wave-uniform
                     buf[slot][i] = __builtin_bit_cast(
-                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, soff, kNonTemporal));
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, soff, KEEP ? 0 : kNonTemporal));
                 });
             };
             static_for<(PF < CTW ? PF : CTW)>([&](auto f) { load_tile(f, f); });
@@ -261,7 +278,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 int j = tile_key(f) + n16;
                 j = j < L ? j : L - 1;
                 const char *a = kb + (int64_t)j * tstride;
-                static_for<NQ>([&](auto qq) { buf[f][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64)); });
+                static_for<NQ>([&](auto qq) { buf[f][qq] = load_key<KEEP>((const u32x4_t *)(a + qq * 64)); });
             });
             static_for<CTW>([&](auto ct) {
                 u32x4_t cur[NQ];
@@ -271,7 +288,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                     j = j < L ? j : L - 1;
                     const char *a = kb + (int64_t)j * tstride;
                     static_for<NQ>([&](auto qq) {
-                        buf[ct % PF][qq] = __builtin_nontemporal_load((const u32x4_t *)(a + qq * 64));
+                        buf[ct % PF][qq] = load_key<KEEP>((const u32x4_t *)(a + qq * 64));
                     });
                 }
                 if constexpr (QLDS) {
@@ -296,7 +313,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             static_for<RTW>([&](auto rt) {
                 static_for<4>([&](auto i) {
                     const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                    const int lim = p.variant == 0 ? P + sh_wrow[row] + 1 : P;  // keys j < lim are visible
+                    const int lim = p.variant == 0 ? P + sh_wrow[cbase + row] + 1 : P;  // keys j < lim are visible
                     static_for<CTW>([&](auto ct) {
                         const int j = tile_key(ct) + n16;
                         if (j >= lim) S[rt][ct][i()] = neg_inf();
@@ -363,12 +380,12 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 static_for<RTW>([&](auto rt) {
                     static_for<4>([&](auto i) {
                         const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                        if (row < p.M) {
+                        if (row < Mc) {
                             // device-coherent store (bypasses the per-XCD L2): the barrier below
                             // needs no cache write-back
-                            const float2 v = make_float2(mrow[rt][i], lrow[rt][i]);
-                            __hip_atomic_store((uint64_t *)&p.partial[(int64_t)s * p.M_pad + row],
-                                               __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                            const float2 st = make_float2(mrow[rt][i], lrow[rt][i]);
+                            __hip_atomic_store((uint64_t *)&p.partial[(int64_t)v * p.M_pad + row],
+                                               __builtin_bit_cast(uint64_t, st), __ATOMIC_RELAXED,
                                                __HIP_MEMORY_SCOPE_AGENT);
                         }
                         sh_rowm[row] = mrow[rt][i];
@@ -420,11 +437,11 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             constexpr int TPR = NT / MROWS;  // threads per row (power of two)
             const int row = tid / TPR, sub = tid - (tid / TPR) * TPR;
             float mm = neg_inf(), ll = 0.f;
-            if (row < p.M) {
+            if (row < Mc) {
                 for (int s2 = sub; s2 < sp.ns; s2 += TPR) {
                     const uint64_t bits = __hip_atomic_load(
-                        (uint64_t *)&p.partial[(int64_t)(sp.seg_slab0 + s2) * p.M_pad + row], __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT);
+                        (uint64_t *)&p.partial[((int64_t)(sp.seg_slab0 + s2) * C + chunk) * p.M_pad + row],
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     const float2 pr = __builtin_bit_cast(float2, bits);
                     merge_stats(mm, ll, pr.x, pr.y, c);
                 }
@@ -437,7 +454,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             }
             if (sub == 0) {
                 const float rm = sh_rowm[row];
-                sh_f[row] = (row < p.M && rm != neg_inf() && ll > 0.f) ? fast_exp2((rm - mm) * c) / ll : 0.f;
+                sh_f[row] = (row < Mc && rm != neg_inf() && ll > 0.f) ? fast_exp2((rm - mm) * c) / ll : 0.f;
             }
             __syncthreads();
         }
@@ -446,8 +463,8 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             if (tid < MROWS) {
                 const int row = tid;
                 float2 mg = make_float2(0.f, 0.f);
-                if (row < p.M) mg = p.merged[(int64_t)seg * p.M_pad + row];
-                const bool ok = row < p.M && mg.x != neg_inf() && mg.y > 0.f;
+                if (row < Mc) mg = p.merged[(int64_t)seg * p.M_pad + row];
+                const bool ok = row < Mc && mg.x != neg_inf() && mg.y > 0.f;
                 sh_rowm[row] = ok ? mg.x : 0.f;
                 sh_f[row] = ok ? 1.f / mg.y : 0.f;
             }
@@ -467,7 +484,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             static_for<RTW>([&](auto rt) {
                 static_for<4>([&](auto i) { f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp + i]; });
             });
-            float *vout = p.votes + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
+            float *vout = p.votes + chunk * p.vplane + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
             static_for<CTW>([&](auto ct) {
                 float v = 0.f;
                 static_for<RTW>([&](auto rt) {
@@ -499,85 +516,80 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     }
 }
 
-// Two-pass path: combine the per-slab stats of every (request, KV head, row).
+// Two-pass path: combine the per-slab stats of every (request, KV head, row chunk, row).
+// grid: (segments * chunks, ceil(chunk rows / 4)); each wave merges one row, its lanes
+// striding over the segment's slabs.
 __global__ void __launch_bounds__(256) merge_stats_kernel(const MergeParams p) {
-    const int seg = blockIdx.x;
+    const int C = p.n_chunks;
+    const int vs = blockIdx.x, seg = vs / C, chunk = vs - (vs / C) * C;
     const int r = seg / p.Hkv, g = seg - (seg / p.Hkv) * p.Hkv;
     const int ns = (p.rt.L[r] + p.slab_keys - 1) / p.slab_keys;
     const int base = p.rt.slab0[r] + g * ns;
-    for (int row = threadIdx.x; row < p.M; row += blockDim.x) {
-        float m = neg_inf(), l = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float2 pr = p.partial[(int64_t)(base + s) * p.M_pad + row];
-            merge_stats(m, l, pr.x, pr.y, p.c);
-        }
-        p.merged[(int64_t)seg * p.M_pad + row] = make_float2(m, l);
+    const int row = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int Mc = p.M - chunk * p.M_pad < p.M_pad ? p.M - chunk * p.M_pad : p.M_pad;
+    if (row >= Mc) return;  // whole wave
+    float m = neg_inf(), l = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+        const float2 pr = p.partial[((int64_t)(base + s) * C + chunk) * p.M_pad + row];
+        merge_stats(m, l, pr.x, pr.y, p.c);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o);
+        merge_stats(m, l, m2, l2, p.c);
+    }
+    if (lane == 0) p.merged[(int64_t)vs * p.M_pad + row] = make_float2(m, l);
 }
+
+// Row-chunked scoring: votes[g][j] = sum over the chunk planes.  grid: (column blocks, H_kv).
+__global__ void __launch_bounds__(256) sum_chunks_kernel(const SumParams p) {
+    const int64_t j = p.col0 + (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= p.col1) return;
+    const int64_t o = (int64_t)blockIdx.y * p.sum_P + j;
+    float a = p.planes[o];
+    for (int c = 1; c < p.n_chunks; ++c) a += p.planes[c * p.vplane + o];
+    p.votes[o] = a;
+}
+const void *sum_kernel() { return (const void *)&sum_chunks_kernel; }
 
 const void *merge_kernel() { return (const void *)&merge_stats_kernel; }
 
 // ---- instantiation table ---------------------------------------------------------------
 
-// Rows of 256 bytes with at most 32 window rows take the register-staged key stream:
-// eight waves, 16 key tiles per wave (128 resident logits per lane).
-constexpr ObsConfig kStagedConfig = {1, 8, 2, 16};
-
-
-bool obs_config(int dtype, int d, int m_pad, ObsConfig *cfg) {
+// Every kernel scores 32 query rows (a row chunk): rows of 256 bytes take the
+// register-staged key stream (eight waves, 16 key tiles per wave), other rows direct
+// MFMA-layout loads.
+bool obs_config(int dtype, int d, ObsConfig *cfg) {
     if (d != 64 && d != 128) return false;
     const int rowb = d * (dtype == 0 ? 4 : 2);
-    ObsConfig c;
-    if (rowb == 256 && m_pad <= 32) {
-        c = kStagedConfig;
-    } else if (rowb <= 256) {
-        if (m_pad <= 32) c = {1, 8, 2, 16};
-        else if (m_pad <= 64) c = {1, 8, 4, 8};
-        else if (m_pad <= 128) c = {2, 4, 4, 8};
-        else if (m_pad <= 256) c = {4, 2, 4, 8};
-        else return false;
-    } else {
-        if (m_pad <= 32) c = {1, 8, 2, 8};
-        else if (m_pad <= 64) c = {2, 4, 2, 8};
-        else if (m_pad <= 128) c = {4, 2, 2, 8};
-        else if (m_pad <= 256) c = {8, 1, 2, 8};
-        else return false;
-    }
-    *cfg = c;
+    *cfg = rowb <= 256 ? ObsConfig{1, 8, 2, 16} : ObsConfig{1, 8, 2, 8};
     return true;
 }
 
-template <typename T, int D, int WR, int WK, int RTW, int CTW, bool STAGED = false>
+template <typename T, int D, int CTW, bool STAGED, bool KEEP>
 static const void *pick_mode(int mode) {
     switch (mode) {
-        case kFused: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kFused, STAGED>;
-        case kStats: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kStats, STAGED>;
-        default: return (const void *)&obs_score_kernel<T, D, WR, WK, RTW, CTW, kVotes, STAGED>;
+        case kFused: return (const void *)&obs_score_kernel<T, D, 1, 8, 2, CTW, kFused, STAGED, KEEP>;
+        case kStats: return (const void *)&obs_score_kernel<T, D, 1, 8, 2, CTW, kStats, STAGED, KEEP>;
+        default: return (const void *)&obs_score_kernel<T, D, 1, 8, 2, CTW, kVotes, STAGED, KEEP>;
     }
+}
+
+template <typename T, int D, bool KEEP>
+static const void *pick_keep(int mode) {
+    if constexpr (D * sizeof(T) == 256) return pick_mode<T, D, 16, true, KEEP>(mode);
+    else if constexpr (D * sizeof(T) < 256) return pick_mode<T, D, 16, false, KEEP>(mode);
+    else return pick_mode<T, D, 8, false, KEEP>(mode);
 }
 
 template <typename T, int D>
-static const void *pick_small_rows(int m_pad, int mode) {  // rows of D*sizeof(T) <= 256 bytes
-    if (m_pad <= 32) {
-        if constexpr (D * sizeof(T) == 256) return pick_mode<T, D, 1, 8, 2, 16, true>(mode);
-        return pick_mode<T, D, 1, 8, 2, 16>(mode);
-    }
-    if (m_pad <= 64) return pick_mode<T, D, 1, 8, 4, 8>(mode);
-    if (m_pad <= 128) return pick_mode<T, D, 2, 4, 4, 8>(mode);
-    return pick_mode<T, D, 4, 2, 4, 8>(mode);
+static const void *pick(int mode, bool keep) {
+    return keep ? pick_keep<T, D, true>(mode) : pick_keep<T, D, false>(mode);
 }
 
-static const void *pick_f32_d128(int m_pad, int mode) {
-    if (m_pad <= 32) return pick_mode<float, 128, 1, 8, 2, 8>(mode);
-    if (m_pad <= 64) return pick_mode<float, 128, 2, 4, 2, 8>(mode);
-    if (m_pad <= 128) return pick_mode<float, 128, 4, 2, 2, 8>(mode);
-    return pick_mode<float, 128, 8, 1, 2, 8>(mode);
-}
-
-const void *obs_kernel(int dtype, int d, int m_pad, int mode) {
-    if (m_pad > 256) return nullptr;
-    if (dtype == 1) return d == 64 ? pick_small_rows<__bf16, 64>(m_pad, mode) : pick_small_rows<__bf16, 128>(m_pad, mode);
-    return d == 64 ? pick_small_rows<float, 64>(m_pad, mode) : pick_f32_d128(m_pad, mode);
+const void *obs_kernel(int dtype, int d, int mode, bool keep) {
+    if (dtype == 1) return d == 64 ? pick<__bf16, 64>(mode, keep) : pick<__bf16, 128>(mode, keep);
+    return d == 64 ? pick<float, 64>(mode, keep) : pick<float, 128>(mode, keep);
 }
 
 }  // namespace snapkv

@@ -60,8 +60,15 @@ struct ObsParams {
     int32_t n_slabs;            // slabs in this group
     int32_t slab_keys;          // keys per slab
     uint32_t spin_limit;        // polls before a barrier wait gives up
+    int32_t n_chunks;           // row chunks of kChunkRows query rows per KV head
+    int64_t vplane;             // floats between the votes planes of consecutive chunks
     ReqTable rt;
 };
+
+// Query rows scored by one kernel pass (a row chunk); heads with more rows (G * L_obs)
+// are scored chunk by chunk into separate votes planes that are then summed.
+constexpr int kChunkRows = 32;
+constexpr int kMaxRows = 1024;  // longest G * L_obs
 
 struct ObsConfig {
     int wr, wk, rtw, ctw;       // waves over rows, waves over keys, 16-row tiles / wave, 16-key tiles / wave
@@ -70,19 +77,27 @@ struct ObsConfig {
     int rows() const { return wr * rtw * 16; }
 };
 
-// Chooses the tile shape for (dtype, d, rows); false if unsupported.
-bool obs_config(int dtype, int d, int m_pad, ObsConfig *cfg);
-// Kernel entry of the chosen instantiation.
-const void *obs_kernel(int dtype, int d, int m_pad, int mode);
+// Chooses the tile shape for (dtype, d); false if unsupported.
+bool obs_config(int dtype, int d, ObsConfig *cfg);
+// Kernel entry of the chosen instantiation; keep = cached key loads.
+const void *obs_kernel(int dtype, int d, int mode, bool keep);
 
 struct MergeParams {
     const float2 *partial;
     float2 *merged;
-    int32_t M, M_pad, slab_keys, Hkv;
+    int32_t M, M_pad, slab_keys, Hkv, n_chunks;
     float c;
     ReqTable rt;
 };
 const void *merge_kernel();
+
+struct SumParams {
+    const float *planes;        // [n_chunks][H_kv][sum_P]
+    float *votes;               // [H_kv][sum_P]
+    int64_t sum_P, vplane, col0, col1;  // columns [col0, col1) of every KV head
+    int32_t n_chunks;
+};
+const void *sum_kernel();
 
 struct PoolParams {
     const float *votes;

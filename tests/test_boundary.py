@@ -72,7 +72,7 @@ BAD = [
     (dict(kv_token_stride=32), "kv_token_stride"),
     (dict(cu_seqlens=np.array([0, 20], np.int32)), "shorter"),
     (dict(cu_seqlens=np.array([5, 1029], np.int32)), "cu_seqlens"),
-    (dict(num_q_heads=48, num_kv_heads=1, obs_window=32), "256"),
+    (dict(num_q_heads=64, num_kv_heads=1, obs_window=17), "1024"),
 ]
 
 

@@ -97,6 +97,9 @@ SMALL = [
     ("pool1_topk_exact", [2000], 2, 2, 128, "bf16", 32, 1, 0.05, None, 8),
     ("varlen_gqa", [33, 2049, 700, 64, 4500], 8, 2, 128, "bf16", 32, 7, 0.05, None, 8),
     ("pool31_half15", [3000], 4, 2, 64, "bf16", 16, 31, 0.05, None, 8),
+    ("gqa_M512_chunks16", [2600], 16, 1, 64, "bf16", 32, 7, 0.05, None, 8),
+    ("gqa_M200_ragged_chunk", [3100, 700], 8, 1, 128, "bf16", 25, 7, 0.05, None, 8),
+    ("f32_d64_M96", [1500], 6, 2, 64, "f32", 32, 5, 0.1, None, 4),
     ("pool17_run32", [20000], 2, 1, 64, "bf16", 16, 17, 0.05, None, 8),
     ("pool33_run32", [20000], 2, 1, 64, "bf16", 16, 33, 0.05, None, 8),
     ("pool41_pool_kernel", [2600, 900], 4, 2, 64, "bf16", 16, 41, 0.05, None, 8),
@@ -236,7 +239,7 @@ def test_workspace_counters_left_zero():
 
 def test_unsupported_rows_raise():
     snap = _snap()
-    wl = synth.custom([600], 16, 1, 64, obs_window=32, pool_kernel=7, ratio=0.05, name="too_many_rows")
+    wl = synth.custom([600], 64, 1, 64, obs_window=17, pool_kernel=7, ratio=0.05, name="too_many_rows")
     x = synth.make_inputs(wl)
     q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
     with pytest.raises(ValueError):
