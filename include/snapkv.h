@@ -182,7 +182,8 @@ typedef enum {
     SNAPKV_K_POOL = 5,        /* vote_pool */
     SNAPKV_K_SELECT = 6,      /* topk_select */
     SNAPKV_K_GATHER = 7,      /* kv_gather */
-    SNAPKV_K_SUM_CHUNKS = 8   /* sum of the votes of the row chunks (G * L_obs > 32) */
+    SNAPKV_K_SUM_CHUNKS = 8,  /* sum of the votes of the row chunks (G * L_obs > 32) */
+    SNAPKV_K_SELECT_TILES = 9 /* topk_select of segments longer than 32768 positions (4 phases) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -51,8 +51,10 @@ struct Plan {
     std::vector<Group> groups;
     int max_group_slabs, max_group_segs;
     int64_t max_P;
+    int max_tiles;     // tiles of the longest segment (long-segment select)
     // workspace layout (bytes)
-    size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx, ws_bytes;
+    size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx;
+    size_t off_long_state, off_ghist, off_cand, off_tilecnt, ws_bytes;
 };
 
 int make_plan(const snapkv_problem *pb, Plan *pl) {
@@ -194,6 +196,17 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     off = align_up(off + sizeof(float) * (size_t)p.Hkv * (size_t)p.sum_P);
     p.off_idx = off;
     off = align_up(off + sizeof(int32_t) * (size_t)p.Hkv * (size_t)p.sum_k);
+    // long-segment select: per-segment state, histograms, candidates, tile counts
+    const bool has_long = p.max_P > select_lds_positions();
+    p.max_tiles = has_long ? (int)((p.max_P + select_tile_positions() - 1) / select_tile_positions()) : 0;
+    p.off_long_state = off;
+    if (has_long) off = align_up(off + sizeof(LongState) * (size_t)p.max_group_segs);
+    p.off_ghist = off;
+    if (has_long) off = align_up(off + sizeof(uint32_t) * 4096 * (size_t)p.max_group_segs);
+    p.off_cand = off;
+    if (has_long) off = align_up(off + sizeof(uint32_t) * (size_t)p.Hkv * (size_t)p.sum_P);
+    p.off_tilecnt = off;
+    if (has_long) off = align_up(off + sizeof(uint32_t) * 4 * (size_t)p.max_tiles * (size_t)p.max_group_segs);
     p.ws_bytes = off;
     return SNAPKV_OK;
 }
@@ -443,31 +456,68 @@ int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, 
     }
 }
 
-// Top-k of every group.  With `votes`, segments that fit in LDS are pooled there first
-// (pooled votes also written to `pooled` if it is not null); longer segments are pooled
-// by the pooling kernel into `pooled`, which must then be given.
-int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, hipStream_t stream) {
+// Whether the select kernels pool the votes themselves: the pool window fits every kernel
+// the group uses (the resident kernel for segments of up to select_lds_positions(), the
+// tile kernel beyond).
+bool select_fuses_pool(const Plan &p, int max_P) {
+    const int m = max_P < select_lds_positions() ? max_P : select_lds_positions();
+    return p.K_pool / 2 <= select_max_half(m);
+}
+
+// Top-k of every group.  With `votes` the select kernels pool first when the window allows
+// (pooled votes also written to `pooled` if it is not null), else the pooling kernel writes
+// `pooled`.  Segments longer than select_lds_positions() need `pooled` (the tile kernel
+// passes the pooled votes between its phases) and the workspace.
+int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, char *ws, hipStream_t stream) {
     for (const Group &gr : p.groups) {
-        const bool in_lds = select_pools(p, gr.max_P);
-        if (votes && !in_lds) {
+        const bool fuse = votes && select_fuses_pool(p, gr.max_P);
+        if (votes && !fuse) {
             int st = run_pool(p, gr, votes, pooled, stream);
             if (st) return st;
         }
-        if (p.cu_k[gr.rt.qi[gr.rt.n - 1] + 1] == p.cu_k[gr.rt.qi[0]] && !(votes && in_lds && pooled)) continue;
-        SelectParams sp;
-        memset(&sp, 0, sizeof sp);
-        sp.votes = (votes && in_lds) ? votes : nullptr;
-        sp.pooled = pooled;
-        sp.pooled_out = (votes && in_lds) ? pooled : nullptr;
-        sp.idx = idx;
-        sp.sum_P = p.sum_P;
-        sp.sum_k = p.sum_k;
-        sp.w = p.w;
-        sp.Hkv = p.Hkv;
-        sp.half = p.K_pool / 2;
-        sp.rt = gr.rt;
-        int st = launch(SNAPKV_K_SELECT, select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp, stream);
-        if (st) return st;
+        const bool any_k = p.cu_k[gr.rt.qi[gr.rt.n - 1] + 1] != p.cu_k[gr.rt.qi[0]];
+        if (any_k || (fuse && pooled)) {
+            SelectParams sp;
+            memset(&sp, 0, sizeof sp);
+            sp.votes = fuse ? votes : nullptr;
+            sp.pooled = pooled;
+            sp.pooled_out = fuse ? pooled : nullptr;
+            sp.idx = idx;
+            sp.sum_P = p.sum_P;
+            sp.sum_k = p.sum_k;
+            sp.w = p.w;
+            sp.Hkv = p.Hkv;
+            sp.half = p.K_pool / 2;
+            sp.rt = gr.rt;
+            int st = launch(SNAPKV_K_SELECT, select_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &sp,
+                            stream);
+            if (st) return st;
+        }
+        if (gr.max_P > select_lds_positions()) {
+            LongParams lp;
+            memset(&lp, 0, sizeof lp);
+            lp.votes = fuse ? votes : nullptr;
+            lp.pooled = pooled;
+            lp.idx = idx;
+            lp.state = (LongState *)(ws + p.off_long_state);
+            lp.ghist = (uint32_t *)(ws + p.off_ghist);
+            lp.cand = (uint32_t *)(ws + p.off_cand);
+            lp.tilecnt = (uint32_t *)(ws + p.off_tilecnt);
+            lp.sum_P = p.sum_P;
+            lp.sum_k = p.sum_k;
+            lp.w = p.w;
+            lp.Hkv = p.Hkv;
+            lp.half = p.K_pool / 2;
+            lp.max_tiles = p.max_tiles;
+            lp.rt = gr.rt;
+            const int tiles = (gr.max_P + select_tile_positions() - 1) / select_tile_positions();
+            for (int phase = 0; phase < 4; ++phase) {
+                lp.phase = phase;
+                int st = launch(SNAPKV_K_SELECT_TILES, long_kernel(), dim3(tiles, gr.rt.n * p.Hkv),
+                                dim3(select_threads()), &lp, stream);
+                if (st) return st;
+            }
+        }
     }
     return SNAPKV_OK;
 }
@@ -562,7 +612,7 @@ int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, v
     DevInfo di;
     st = device_info(&di);
     if (st) return st;
-    return finish(run_select(p, nullptr, (float *)pooled, idx, (hipStream_t)stream));
+    return finish(run_select(p, nullptr, (float *)pooled, idx, (char *)ws, (hipStream_t)stream));
 }
 
 int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const int32_t *idx, void *K_out,
@@ -598,10 +648,11 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
     hipStream_t s = (hipStream_t)stream;
     float *votes = (float *)(w + p.off_votes);
     // pooled votes: the caller's buffer, or workspace when long segments need them in memory
-    float *pl = pooled ? pooled : (!select_pools(p, p.max_P) ? (float *)(w + p.off_pooled) : nullptr);
+    const bool need_pooled = p.max_P > select_lds_positions() || !select_fuses_pool(p, p.max_P);
+    float *pl = pooled ? pooled : (need_pooled ? (float *)(w + p.off_pooled) : nullptr);
     int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
     st = run_scores(p, q_obs, K, votes, nullptr, false, w, s);
-    if (!st) st = run_select(p, votes, pl, ix, s);
+    if (!st) st = run_select(p, votes, pl, ix, w, s);
     if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s);
     return finish(st);
 }
@@ -636,6 +687,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_SELECT: return "topk_select";
         case SNAPKV_K_GATHER: return "kv_gather";
         case SNAPKV_K_SUM_CHUNKS: return "sum_chunks";
+        case SNAPKV_K_SELECT_TILES: return "topk_select_tiles";
         default: return "unknown";
     }
 }

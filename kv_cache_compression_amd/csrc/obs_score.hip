@@ -179,12 +179,12 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     for (int r = tid; r < kMaxRows; r += NT) sh_wrow[r] = r % p.w;
     __syncthreads();
 
-    // Work items are (slab, row chunk) pairs, chunk fastest.  With a grid that is a multiple
-    // of 8, consecutive items go to workgroups b, b+8, b+16, ... which the dispatcher places
-    // on one XCD, so the chunks of a slab read it from that XCD's L2.
+    // Work items are (slab, row chunk) pairs, chunk fastest.  With several chunks and a grid
+    // that is a multiple of 8, consecutive items go to workgroups b, b+8, b+16, ... which the
+    // dispatcher places on one XCD, so the chunks of a slab read it from that XCD's L2.
     const int C = p.n_chunks;
     const int nb = gridDim.x;
-    const int b0 = (nb & 7) ? (int)blockIdx.x : ((int)blockIdx.x & 7) * (nb >> 3) + ((int)blockIdx.x >> 3);
+    const int b0 = (C == 1 || (nb & 7)) ? (int)blockIdx.x : ((int)blockIdx.x & 7) * (nb >> 3) + ((int)blockIdx.x >> 3);
     for (int v = b0; v < p.n_slabs * C; v += nb) {
         const int s = v / C, chunk = v - (v / C) * C;
         const SlabPos sp = decode_slab(p.rt, s, SLAB);

@@ -49,6 +49,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelLds = 32768;
 constexpr int kBins = 2048;
+constexpr int kSelMaxHalfAll = 16;  // widest pool half-width pooled in any select kernel
 // Widest pool half-width (K_pool / 2) pooled inside the select kernel for runs of R
 // positions per thread (the pooling window of a run is held in registers).
 constexpr int max_half(int R) { return R <= 16 ? 16 : 8; }
@@ -72,23 +73,21 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
-// Histogram slot of a digit.  Bins are stored in descending digit order q = 2047 - digit,
-// with the 16-byte chunks of each 32-bin block rotated by the block number so that wave 0's
-// reads of one block per lane spread over the LDS banks.
-__device__ __forceinline__ uint32_t hist_slot(uint32_t digit) {
-    const uint32_t q = (kBins - 1) - digit;
-    return q ^ ((q >> 3) & 0x1Cu);
-}
-
-// Wave 0: the bin that holds the need-th largest remaining value.  Lane l sums descending
-// bins q = 32l .. 32l+31; a wave scan finds the block, then lanes 0..31 take one bin each
-// of that block and a second scan finds the bin.  Writes (digit, count above the bin,
-// count in the bin) to sh; writes nothing if no bin qualifies (inputs outside the contract).
+// Wave 0: the bin that holds the need-th largest remaining value of a histogram of NB
+// bins (NB = 64 * BPL, bin = digit, ascending).  Lane l sums the BPL bins of descending
+// block l (digits NB-1-BPL*l down to NB-BPL*(l+1)), reading its 16-byte chunks in a
+// lane-rotated order so the lanes spread over the LDS banks; a wave scan finds the block,
+// then lane j < BPL takes one bin of it and a second scan finds the bin.  Writes (digit,
+// count above the bin, count in the bin) to sh; nothing if no bin qualifies (inputs
+// outside the contract).
+template <int NB>
 __device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t need, uint32_t *sh) {
+    constexpr int BPL = NB / 64, CH = BPL / 4;
     const int lane = threadIdx.x & 63;
+    const uint32_t *blk = hist + NB - BPL * (lane + 1);
     uint32_t sum = 0;
-    static_for<8>([&](auto m) {
-        const u32x4_t t = *(const u32x4_t *)(hist + 32 * lane + 4 * (m() ^ (lane & 7)));
+    static_for<CH>([&](auto m) {
+        const u32x4_t t = *(const u32x4_t *)(blk + 4 * ((m() + lane) & (CH - 1)));
         sum += t.x + t.y + t.z + t.w;
     });
     const uint32_t incl = wave_incl_scan(sum);
@@ -96,16 +95,13 @@ __device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t need, ui
     if (!hit) return;
     const int L = __ffsll((unsigned long long)hit) - 1;
     const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)(incl - sum), L);
-    uint32_t c = 0;
-    if (lane < 32) {
-        const uint32_t q = 32 * L + lane;
-        c = hist[q ^ ((q >> 3) & 0x1Cu)];
-    }
+    const int digit = NB - 1 - (BPL * L + lane);
+    const uint32_t c = lane < BPL ? hist[digit] : 0u;
     const uint32_t ci = above + wave_incl_scan(c);
-    const uint64_t hit2 = __ballot(lane < 32 && ci - c < need && need <= ci);
+    const uint64_t hit2 = __ballot(lane < BPL && ci - c < need && need <= ci);
     if (!hit2) return;
     if (lane == __ffsll((unsigned long long)hit2) - 1) {
-        sh[0] = (uint32_t)(kBins - 1 - (32 * L + lane));
+        sh[0] = (uint32_t)digit;
         sh[1] = ci - c;
         sh[2] = c;
     }
@@ -132,9 +128,9 @@ constexpr int ilog2(int x) { return x >= 32 ? 5 : x >= 16 ? 4 : x >= 8 ? 3 : x >
 // doubling steps make a[i] the max over [i, i + PW), PW the largest power of two <= 2H+1,
 // and each output is the max of two such spans that together cover its window.
 // Positions outside [0, P) read as 0, which never wins a max of values >= 0 whose window
-// contains the position itself.
+// contains the position itself.  Position pos sits at sdata[pos + off].
 template <int R, int H>
-__device__ __forceinline__ void pool_run(const uint32_t *sdata, int P, int j0, uint32_t (&u)[R]) {
+__device__ __forceinline__ void pool_run(const uint32_t *sdata, int P, int j0, uint32_t (&u)[R], int off = 0) {
     constexpr int SUB = R < 8 ? R : 8;  // outputs per block (bounds the registers in flight)
     constexpr int HM = (H + 3) / 4 * 4;
     constexpr int N = SUB + 2 * HM;
@@ -145,7 +141,7 @@ __device__ __forceinline__ void pool_run(const uint32_t *sdata, int P, int j0, u
         static_for<N / 4>([&](auto c) {
             const int pos = b0 - HM + 4 * c();
             u32x4_t t = {0u, 0u, 0u, 0u};
-            if (pos >= 0 && pos < P) t = *(const u32x4_t *)(sdata + pos);
+            if (pos >= 0 && pos < P) t = *(const u32x4_t *)(sdata + pos + off);
             a[4 * c() + 0] = pos + 0 < P ? t.x : 0u;
             a[4 * c() + 1] = pos + 1 < P ? t.y : 0u;
             a[4 * c() + 2] = pos + 2 < P ? t.z : 0u;
@@ -196,19 +192,22 @@ struct SelectShared {
 };
 
 // Exclusive prefix sum of x over the workgroup (one barrier); *total gets the sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t *total, SelectShared &s) {
+__device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t x, uint32_t *total, uint32_t *wtot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(x);
-    if (lane == 63) s.wtot[wave] = incl;
+    if (lane == 63) wtot[wave] = incl;
     __syncthreads();
     uint32_t woff = 0, tot = 0;
     static_for<kSelWaves>([&](auto w2) {
-        const uint32_t t = s.wtot[w2()];
+        const uint32_t t = wtot[w2()];
         woff += w2() < wave ? t : 0u;
         tot += t;
     });
     *total = tot;
     return woff + incl - x;
+}
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t *total, SelectShared &s) {
+    return block_excl_scan_t(x, total, s.wtot);
 }
 
 // One radix step: histogram of the digit (v >> shift) & dmask over values matching the
@@ -218,11 +217,11 @@ template <typename Vals>
 __device__ __forceinline__ bool radix_step(Vals &&for_each_value, int shift, uint32_t dmask, uint32_t *h,
                                            bool clear0, Pivot &pv, SelectShared &s) {
     for_each_value([&](uint32_t v) {
-        if ((v & pv.mask) == pv.prefix) atomicAdd(&h[hist_slot((v >> shift) & dmask)], 1u);
+        if ((v & pv.mask) == pv.prefix) atomicAdd(&h[(v >> shift) & dmask], 1u);
     });
     __syncthreads();
     if (threadIdx.x < 64) {
-        find_bin(h, pv.need, s.sh);
+        find_bin<kBins>(h, pv.need, s.sh);
     } else if (clear0) {
         for (int i = threadIdx.x - 64; i < kBins; i += kSelThreads - 64) s.hist[0][i] = 0;
     }
@@ -348,78 +347,274 @@ __device__ __forceinline__ void select_resident(const SelectParams &p, uint32_t 
     });
 }
 
-// Global path for segments longer than kSelLds: each pass re-reads the pooled votes.
-__device__ __forceinline__ void select_global(const uint32_t *__restrict__ src, int P, int k, int32_t *__restrict__ out,
-                              SelectShared &s) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < 2 * kBins; i += kSelThreads) (&s.hist[0][0])[i] = 0;
-    __syncthreads();
-    Pivot pv = {0u, 0u, (uint32_t)k};
-    bool done = false;
-    static_for<3>([&](auto pass) {
-        if (done) return;
-        constexpr int PASS = decltype(pass)::value;
-        using D = Digit<PASS>;
-        uint32_t *h = s.hist[PASS & 1];
-        for (int j0 = 0; j0 < P; j0 += 4 * kSelThreads) {
-            const int j = j0 + 4 * tid;
-            uint32_t v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = j + e < P ? src[j + e] : 0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j + e < P && (v[e] & pv.mask) == pv.prefix) atomicAdd(&h[hist_slot((v[e] >> D::shift) & D::mask)], 1u);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            find_bin(h, pv.need, s.sh);
-        } else if (PASS == 1) {
-            for (int i = tid - 64; i < kBins; i += kSelThreads - 64) s.hist[0][i] = 0;
-        }
-        __syncthreads();
-        const uint32_t dg = s.sh[0], above = s.sh[1], cnt = s.sh[2];
-        pv.prefix |= dg << D::shift;
-        pv.mask |= D::mask << D::shift;
-        pv.need -= above;
-        done = cnt == pv.need;
-    });
+// ---- segments longer than kSelLds -----------------------------------------------------------
+// Tiles of kTile positions, one workgroup each, in four launches (phase 0..3):
+//   0: pool the tile (halo from the neighbours' votes), write the pooled votes, add a
+//      4096-bin histogram of bits 30..19 to the segment's global histogram; the tile that
+//      finishes last picks the bin b of the k-th value and clears the histogram.
+//   1: each tile counts its values above bin b, records that count, and appends its values
+//      in bin b to the segment's candidate list (recording where); the last tile refines
+//      the exact k-th value among the candidates (bits 18..8, then 7..0).
+//   2: each tile's counts above / equal to that value, from its record and its candidates.
+//   3: each tile adds the counts of the tiles before it and writes its positions in order.
+// "Last" is decided by a per-segment arrival counter that the last tile resets, so no
+// workgroup ever waits for another.  Full passes over the tile use coalesced loads (LDS
+// holds the tile where a thread needs its own contiguous run).
+constexpr int kTile = 16 * kSelThreads;
+constexpr int kLongBins = 4096;
+int select_tile_positions() { return kTile; }
 
-    // ordered compaction in chunks of 4 * kSelThreads positions (4 consecutive per thread)
-    uint32_t base_gt = 0, base_eq = 0;
-    for (int j0 = 0; j0 < P; j0 += 4 * kSelThreads) {
-        const int j = j0 + 4 * tid;
-        uint32_t m[4];
-        uint32_t packed = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            m[e] = (j + e < P ? src[j + e] : 0u) & pv.mask;
-            if (j + e < P) packed += m[e] > pv.prefix ? 1u : (m[e] == pv.prefix ? 0x10000u : 0u);
-        }
-        const uint32_t incl = wave_incl_scan(packed);
-        if (lane == 63) s.wtot[wave] = incl;
-        __syncthreads();
-        uint32_t woff = 0, ctot = 0;
-        static_for<kSelWaves>([&](auto w2) {
-            const uint32_t t = s.wtot[w2()];
-            woff += w2() < wave ? t : 0u;
-            ctot += t;
-        });
-        const uint32_t excl = woff + incl - packed;
-        uint32_t gt_before = base_gt + (excl & 0xFFFFu), eq_before = base_eq + (excl >> 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool gt = j + e < P && m[e] > pv.prefix, eq = j + e < P && m[e] == pv.prefix;
-            const uint32_t taken = eq_before < pv.need ? eq_before : pv.need;
-            if ((gt || (eq && eq_before < pv.need)) && gt_before + taken < (uint32_t)k) out[gt_before + taken] = j + e;
-            gt_before += gt ? 1u : 0u;
-            eq_before += eq ? 1u : 0u;
-        }
-        base_gt += ctot & 0xFFFFu;
-        base_eq += ctot >> 16;
-        __syncthreads();
-        if (base_gt + (base_eq < pv.need ? base_eq : pv.need) >= (uint32_t)k) break;  // all k written
+struct LongShared {
+    uint32_t hist[kLongBins];
+    uint32_t sh[4];
+    uint32_t wtot[kSelWaves];
+    uint32_t last;
+};
+
+// Block-wide: arrival of this tile at the segment's counter; true in every thread of the
+// tile that arrived last (whose arrival also resets the counter for the next call).
+__device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t n_tiles, LongShared &s) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = before == n_tiles - 1;
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s.last = last ? 1u : 0u;
     }
+    __syncthreads();
+    return s.last != 0;
 }
+
+// Coalesced load of the tile's values: position start + i * kSelThreads + tid at u[i].
+__device__ __forceinline__ void load_tile_strided(const uint32_t *src, int P, int start, uint32_t (&u)[16]) {
+    static_for<16>([&](auto i) {
+        const int j = start + i() * kSelThreads + (int)threadIdx.x;
+        u[i()] = j < P ? src[j] : 0u;
+    });
+}
+
+__global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams p) {
+    constexpr int HA = kSelMaxHalfAll;
+    __shared__ __attribute__((aligned(16))) uint32_t sdata[kTile + 2 * HA];
+    __shared__ __attribute__((aligned(16))) LongShared s;
+    const int tid = threadIdx.x;
+    const int seg = blockIdx.y;
+    const int r = seg / p.Hkv, g = seg - (seg / p.Hkv) * p.Hkv;
+    const int P = p.rt.L[r] - p.w;
+    const int k = p.rt.k[r];
+    const int start = blockIdx.x * kTile;
+    if (P <= kSelLds || start >= P || (p.phase > 0 && (k <= 0 || k >= P))) return;  // whole workgroup
+    const uint32_t n_tiles = (uint32_t)((P + kTile - 1) / kTile);
+    const int64_t base = (int64_t)g * p.sum_P + p.rt.pfx0[r];
+    LongState *st = p.state + seg;
+    uint32_t *rec = p.tilecnt + ((int64_t)seg * p.max_tiles + blockIdx.x) * 4;  // tile record
+    int32_t *out = p.idx + (int64_t)g * p.sum_k + p.rt.k0[r];
+    const int j0 = start + 16 * tid;
+    const int nvalid = P - j0 < 0 ? 0 : (P - j0 > 16 ? 16 : P - j0);
+    const int off = HA - start;  // position pos sits at sdata[pos + off]
+
+    if (p.phase == 0) {
+        // stage votes [start - HA, start + kTile + HA)
+        const uint32_t *src = (const uint32_t *)((p.votes ? p.votes : p.pooled) + base);
+        uint32_t t[16];
+        load_tile_strided(src, P, start, t);
+        uint32_t h0 = 0, h1 = 0;
+        if (tid < HA) {
+            const int jl = start - HA + tid, jr = start + kTile + tid;
+            h0 = jl >= 0 ? src[jl] : 0u;
+            h1 = jr < P ? src[jr] : 0u;
+        }
+        for (int i = tid; i < kLongBins; i += kSelThreads) s.hist[i] = 0;
+        static_for<16>([&](auto i) { sdata[i() * kSelThreads + tid + HA] = t[i()]; });
+        if (tid < HA) {
+            sdata[tid] = h0;
+            sdata[kTile + HA + tid] = h1;
+        }
+        __syncthreads();
+        uint32_t u[16];
+        if (p.votes) {
+            static_for<HA + 1>([&](auto h) {
+                if (p.half == decltype(h)::value) pool_run<16, decltype(h)::value>(sdata, P, j0, u, off);
+            });
+            // pooled run -> LDS -> coalesced stores
+            __syncthreads();
+            static_for<16>([&](auto i) { sdata[16 * tid + i() + HA] = u[i()]; });
+            __syncthreads();
+            uint32_t *dst = (uint32_t *)(p.pooled + base);
+            static_for<16>([&](auto i) {
+                const int j = start + i() * kSelThreads + tid;
+                if (j < P) dst[j] = sdata[i() * kSelThreads + tid + HA];
+            });
+        } else {
+            static_for<16>([&](auto i) { u[i()] = sdata[16 * tid + i() + HA]; });
+        }
+        if (k <= 0) return;
+        if (k >= P) {  // every position, in order
+            static_for<16>([&](auto i) {
+                if (i() < nvalid) out[j0 + i()] = j0 + i();
+            });
+            return;
+        }
+        static_for<16>([&](auto i) {
+            if (i() < nvalid) atomicAdd(&s.hist[(u[i()] & 0x7FFFFFFFu) >> 19], 1u);
+        });
+        __syncthreads();
+        uint32_t *gh = p.ghist + (int64_t)seg * kLongBins;
+        for (int i = tid; i < kLongBins; i += kSelThreads)
+            if (s.hist[i]) __hip_atomic_fetch_add(&gh[i], s.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!arrive_last(&st->arrived, n_tiles, s)) return;
+        // last tile: the segment's histogram -> LDS (and cleared for the next call)
+        for (int i = tid; i < kLongBins; i += kSelThreads) {
+            s.hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (tid < 64) find_bin<kLongBins>(s.hist, (uint32_t)k, s.sh);
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t need = (uint32_t)k - s.sh[1];
+            st->prefix = s.sh[0] << 19;
+            st->mask = 0xFFFu << 19;
+            st->need = need;
+            st->done = need == s.sh[2] ? 1u : 0u;  // the whole bin is taken
+            st->ncand = 0;
+        }
+        return;
+    }
+
+    const uint32_t *src = (const uint32_t *)(p.pooled + base);
+    const int lane = tid & 63, wave = tid >> 6;
+    if (p.phase == 1) {
+        const uint32_t prefix = st->prefix, mask = st->mask;
+        const bool refine = st->done == 0;
+        uint32_t u[16];
+        load_tile_strided(src, P, start, u);
+        uint32_t gt = 0, c = 0;
+        static_for<16>([&](auto i) {
+            const int j = start + i() * kSelThreads + tid;
+            const uint32_t m = u[i()] & 0x7FFFFFFFu & mask;
+            gt += (j < P && m > prefix) ? 1u : 0u;
+            c += (j < P && m == prefix) ? 1u : 0u;
+        });
+        uint32_t gtot, ctot;
+        (void)block_excl_scan_t(gt, &gtot, s.wtot);
+        __syncthreads();
+        const uint32_t cexcl = block_excl_scan_t(c, &ctot, s.wtot);
+        if (tid == 0) {
+            const uint32_t o0 = refine ? __hip_atomic_fetch_add(&st->ncand, ctot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+            s.sh[3] = o0;
+            rec[0] = gtot;
+            rec[1] = o0;
+            rec[2] = ctot;
+        }
+        if (!refine) return;
+        __syncthreads();
+        uint32_t *cand = p.cand + base;
+        uint32_t o = s.sh[3] + cexcl;
+        static_for<16>([&](auto i) {
+            const int j = start + i() * kSelThreads + tid;
+            const uint32_t v = u[i()] & 0x7FFFFFFFu;
+            if (j < P && (v & mask) == prefix) __hip_atomic_store(&cand[o++], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        });
+        if (!arrive_last(&st->arrived, n_tiles, s)) return;
+        // last tile: the exact k-th value among the candidates
+        const int ncand = (int)__hip_atomic_load(&st->ncand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        Pivot pv = {prefix, mask, st->need};
+        static_for<2>([&](auto pass) {
+            constexpr int shift = decltype(pass)::value == 0 ? 8 : 0;
+            constexpr uint32_t dmask = decltype(pass)::value == 0 ? 0x7FFu : 0xFFu;
+            for (int i = tid; i < kLongBins; i += kSelThreads) s.hist[i] = 0;
+            __syncthreads();
+            for (int i0 = tid; i0 < ncand; i0 += 8 * kSelThreads) {  // eight loads in flight
+                uint32_t v[8];
+                static_for<8>([&](auto e) {
+                    const int i = i0 + e() * kSelThreads;
+                    v[e()] = i < ncand ? __hip_atomic_load(&cand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+                });
+                static_for<8>([&](auto e) {
+                    if (i0 + e() * kSelThreads < ncand && (v[e()] & pv.mask) == pv.prefix)
+                        atomicAdd(&s.hist[(v[e()] >> shift) & dmask], 1u);
+                });
+            }
+            __syncthreads();
+            if (tid < 64) find_bin<kBins>(s.hist, pv.need, s.sh);
+            __syncthreads();
+            pv.prefix |= s.sh[0] << shift;
+            pv.mask |= dmask << shift;
+            pv.need -= s.sh[1];
+            __syncthreads();
+        });
+        if (tid == 0) {
+            st->prefix = pv.prefix;
+            st->mask = pv.mask;
+            st->need = pv.need;
+        }
+        return;
+    }
+
+    const uint32_t prefix = st->prefix, mask = st->mask, need = st->need;
+    if (p.phase == 2) {
+        // counts above / equal to the pivot: the values above the first bin, plus this
+        // tile's candidates (all of them when the first bin was taken whole)
+        uint32_t gt = 0, eq = 0;
+        const uint32_t o0 = rec[1], nc = rec[2];
+        if (st->done) {
+            eq = tid == 0 ? nc : 0u;
+        } else {
+            const uint32_t *cand = p.cand + base;
+            for (uint32_t i = tid; i < nc; i += kSelThreads) {
+                const uint32_t m = cand[o0 + i] & mask;
+                gt += m > prefix ? 1u : 0u;
+                eq += m == prefix ? 1u : 0u;
+            }
+        }
+        uint32_t gtot, etot;
+        (void)block_excl_scan_t(gt, &gtot, s.wtot);
+        __syncthreads();
+        (void)block_excl_scan_t(eq, &etot, s.wtot);
+        if (tid == 0) rec[3] = ((rec[0] + gtot) & 0xFFFFu) | (etot << 16);
+        return;
+    }
+
+    // phase 3: ordered writes after the counts of the tiles before this one
+    {
+        uint32_t t[16];
+        load_tile_strided(src, P, start, t);
+        static_for<16>([&](auto i) { sdata[i() * kSelThreads + tid] = t[i()]; });
+    }
+    uint32_t pgt = 0, peq = 0;
+    const uint32_t *recs = p.tilecnt + (int64_t)seg * p.max_tiles * 4;
+    for (int t = tid; t < (int)blockIdx.x; t += kSelThreads) {
+        const uint32_t v = recs[4 * t + 3];
+        pgt += v & 0xFFFFu;
+        peq += v >> 16;
+    }
+    uint32_t gt_base, eq_base;
+    (void)block_excl_scan_t(pgt, &gt_base, s.wtot);
+    __syncthreads();
+    (void)block_excl_scan_t(peq, &eq_base, s.wtot);  // its barrier also publishes sdata
+    __syncthreads();
+    uint32_t u[16];
+    static_for<16>([&](auto i) { u[i()] = sdata[16 * tid + i()] & 0x7FFFFFFFu; });
+    uint32_t packed = 0;
+    static_for<16>([&](auto i) {
+        const uint32_t m = u[i()] & mask;
+        if (i() < nvalid) packed += m > prefix ? 1u : (m == prefix ? 0x10000u : 0u);
+    });
+    uint32_t total;
+    const uint32_t excl = block_excl_scan_t(packed, &total, s.wtot);
+    uint32_t gt_before = gt_base + (excl & 0xFFFFu), eq_before = eq_base + (excl >> 16);
+    static_for<16>([&](auto i) {
+        const uint32_t m = u[i()] & mask;
+        const bool gt = i() < nvalid && m > prefix, eq = i() < nvalid && m == prefix;
+        const uint32_t taken = eq_before < need ? eq_before : need;
+        if ((gt || (eq && eq_before < need)) && gt_before + taken < (uint32_t)k) out[gt_before + taken] = j0 + i();
+        gt_before += gt ? 1u : 0u;
+        eq_before += eq ? 1u : 0u;
+    });
+}
+const void *long_kernel() { return (const void *)&topk_long_kernel; }
 
 __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(const SelectParams p) {
     __shared__ __attribute__((aligned(16))) uint32_t sdata[kSelLds];
@@ -437,15 +632,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(const SelectPa
         else if (P <= 8 * kSelThreads) select_resident<8>(p, sdata, s, P, k, base, out);
         else if (P <= 16 * kSelThreads) select_resident<16>(p, sdata, s, P, k, base, out);
         else select_resident<32>(p, sdata, s, P, k, base, out);
-    } else {
-        // long segment: pooled by the pooling kernel, read from global memory on each pass
-        if (!out || k <= 0) return;
-        if (k >= P) {
-            for (int j = threadIdx.x; j < P; j += kSelThreads) out[j] = j;
-            return;
-        }
-        select_global((const uint32_t *)(p.pooled + base), P, k, out, s);
-    }
+    }  // longer segments: topk_long_kernel
 }
 const void *select_kernel() { return (const void *)&topk_select_kernel; }
 

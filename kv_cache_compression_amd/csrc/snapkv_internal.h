@@ -122,6 +122,30 @@ int select_threads();
 int select_lds_positions();     // longest segment selected from LDS / registers
 int select_max_half(int max_P); // widest pool half-width (K_pool / 2) the select kernel pools itself
 
+// Per-segment state of the long-segment select (64 bytes; zero in a fresh workspace, and
+// the counters return to zero after every call).
+struct LongState {
+    uint32_t arrived;           // tiles arrived in the current phase
+    uint32_t ncand;             // candidates appended in phase 1
+    uint32_t prefix, mask, need, done;
+    uint32_t pad[10];
+};
+
+struct LongParams {
+    const float *votes;         // raw votes to pool in phase 0, or null (pooled given)
+    float *pooled;              // pooled votes: written in phase 0 when votes is set, read after
+    int32_t *idx;
+    LongState *state;           // [segments]
+    uint32_t *ghist;            // [segments][4096]
+    uint32_t *cand;             // [H_kv][sum_P] candidate values
+    uint32_t *tilecnt;          // [segments][max_tiles][4]: above first bin, candidate start, count, packed counts
+    int64_t sum_P, sum_k;
+    int32_t w, Hkv, half, phase, max_tiles;
+    ReqTable rt;
+};
+const void *long_kernel();
+int select_tile_positions();
+
 struct GatherParams {
     const void *K, *V;
     const int32_t *idx;
