@@ -10,6 +10,8 @@ NumPy-facing wrapper that builds and loads it.
 from .ref import (  # noqa: F401
     build,
     votes,
+    row_lse,
+    lse_all,
     pool,
     k_of,
     select,

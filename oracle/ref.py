@@ -67,6 +67,8 @@ def _load():
             vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
             lib.snapkv_oracle_votes.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i64, i64, i32, vp, vp]
             lib.snapkv_oracle_votes.restype = None
+            lib.snapkv_oracle_row_lse.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i64, i64, i32, vp, vp]
+            lib.snapkv_oracle_row_lse.restype = None
             lib.snapkv_oracle_pool.argtypes = [vp, i64, i32, vp]
             lib.snapkv_oracle_pool.restype = None
             lib.snapkv_oracle_k.argtypes = [i64, i32, dbl, i64]
@@ -114,6 +116,35 @@ def votes(q: np.ndarray, keys: np.ndarray, w: int, variant: int = 0) -> np.ndarr
     row_buf = np.empty(max(L, 1), np.float64)
     _load().snapkv_oracle_votes(_ptr(q), dt, q.shape[0], w, q.shape[1], _ptr(keys),
                                 keys.strides[0] // keys.itemsize, L, variant, _ptr(out), _ptr(row_buf))
+    return out
+
+
+def row_lse(q: np.ndarray, keys: np.ndarray, w: int, variant: int = 0) -> np.ndarray:
+    """Log-sum-exp of each window row's logits over the keys it sees (the softmax
+    denominator of section 投票メカニズム in log form); rows as in votes().  float64 [G*w]."""
+    q = np.ascontiguousarray(q)
+    if keys.strides[1] != keys.itemsize:
+        keys = np.ascontiguousarray(keys)
+    dt = _dtype_code(q)
+    assert _dtype_code(keys) == dt and q.shape[1] == keys.shape[1] and q.shape[0] % w == 0
+    L = keys.shape[0]
+    out = np.empty(q.shape[0], np.float64)
+    row_buf = np.empty(max(L, 1), np.float64)
+    _load().snapkv_oracle_row_lse(_ptr(q), dt, q.shape[0], w, q.shape[1], _ptr(keys),
+                                  keys.strides[0] // keys.itemsize, L, variant, _ptr(out), _ptr(row_buf))
+    return out
+
+
+def lse_all(q_obs: np.ndarray, K: np.ndarray, cu_seqlens, w: int, variant: int = 0) -> np.ndarray:
+    """row_lse for every request and query head: float64 [B, H_q, w] (q_obs [B, H_q, w, d],
+    K [H_kv, T, d]; query head h reads KV head h // G)."""
+    B, Hq = q_obs.shape[0], q_obs.shape[1]
+    G = Hq // K.shape[0]
+    out = np.empty((B, Hq, w), np.float64)
+    for r in range(B):
+        t0, t1 = int(cu_seqlens[r]), int(cu_seqlens[r + 1])
+        for h in range(Hq):
+            out[r, h] = row_lse(q_obs[r, h], K[h // G, t0:t1], w, variant)
     return out
 
 

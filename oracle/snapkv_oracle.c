@@ -104,6 +104,37 @@ void snapkv_oracle_votes(const void *q, int dtype, int64_t n_rows, int32_t w, in
 }
 
 /*
+ * Log-sum-exp of each window row's logits over the keys it sees (the softmax
+ * denominator of 投票メカニズム and of the アルゴリズム listing's softmax, in log
+ * form): lse[r] = ln sum_j exp(q_r . k_j / sqrt(d)), -infinity for a row that
+ * sees no key.  Same visibility rule and row numbering as snapkv_oracle_votes.
+ */
+void snapkv_oracle_row_lse(const void *q, int dtype, int64_t n_rows, int32_t w, int32_t d,
+                           const void *keys, int64_t key_stride, int64_t L, int32_t variant,
+                           double *lse, double *row_buf)
+{
+    int64_t P = L - w;
+    double scale = 1.0 / sqrt((double)d);
+    for (int64_t r = 0; r < n_rows; ++r) {
+        int64_t i = r % w;
+        int64_t n_vis = variant == 0 ? P + i + 1 : P;
+        if (n_vis <= 0) { lse[r] = -INFINITY; continue; }
+        const void *qr = row_ptr(q, dtype, r, d);
+        for (int64_t j = 0; j < n_vis; ++j) {
+            const void *kj = row_ptr(keys, dtype, j, key_stride);
+            double s = 0.0;
+            for (int32_t c = 0; c < d; ++c) s += widen(qr, dtype, c) * widen(kj, dtype, c);
+            row_buf[j] = s * scale;
+        }
+        double m = row_buf[0];
+        for (int64_t j = 1; j < n_vis; ++j) if (row_buf[j] > m) m = row_buf[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < n_vis; ++j) l += exp(row_buf[j] - m);
+        lse[r] = m + log(l);
+    }
+}
+
+/*
  * 1-D max pooling of width K_pool (odd), stride 1, padding K_pool/2 with
  * -infinity, over C[0..P).  Section クラスタリングによる文脈保持; the
  * アルゴリズム listing's pooling call.

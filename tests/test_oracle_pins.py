@@ -318,3 +318,46 @@ def test_window_only_request():
     x = synth.make_inputs(wl)
     res = oracle.compress(x["q_obs"], x["K"], x["V"], x["cu_seqlens"], 8, 3, ratio=0.5)
     assert res[(0, 0)]["k"] == 0 and res[(0, 0)]["K_out"].tobytes() == x["K"][0].tobytes()
+
+
+# ---- row log-sum-exp (input of the LSE-fed path) ----------------------------------------------
+
+def test_row_lse_uniform_logits_closed_form():
+    """q = 0: every visible logit is 0, so lse_i = ln(#visible keys): ln(P + i + 1) with the
+    causal window, ln(P) for the prefix-only variant."""
+    rng = np.random.default_rng(7)
+    w, d, L = 4, 8, 23
+    q = np.zeros((2 * w, d), np.float32)
+    keys = rng.standard_normal((L, d)).astype(np.float32)
+    P = L - w
+    lse = oracle.row_lse(q, keys, w, variant=0)
+    np.testing.assert_allclose(lse, [np.log(P + (r % w) + 1) for r in range(2 * w)], rtol=0, atol=1e-12)
+    lse1 = oracle.row_lse(q, keys, w, variant=1)
+    np.testing.assert_allclose(lse1, np.full(2 * w, np.log(P)), rtol=0, atol=1e-12)
+
+
+def test_row_lse_one_row_matches_scipy_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(8)
+    d, L = 16, 40
+    q = rng.standard_normal((1, d)).astype(np.float32)
+    keys = (3 * rng.standard_normal((L, d))).astype(np.float32)
+    s = keys.astype(np.float64) @ q[0].astype(np.float64) / np.sqrt(d)
+    np.testing.assert_allclose(oracle.row_lse(q, keys, 1), [logsumexp(s)], rtol=1e-13)
+
+
+def test_row_lse_normalises_the_votes():
+    """exp(s_ij - lse_i) summed over rows i equals the vote of every key (votes() computes its
+    normaliser separately, from the row max and sum)."""
+    rng = np.random.default_rng(9)
+    w, d, L = 3, 8, 17
+    q = rng.standard_normal((2 * w, d)).astype(np.float32)
+    keys = rng.standard_normal((L, d)).astype(np.float32)
+    lse = oracle.row_lse(q, keys, w)
+    P = L - w
+    s = (q.astype(np.float64) @ keys.astype(np.float64).T) / np.sqrt(d)
+    v = np.zeros(L)
+    for r in range(2 * w):
+        n = P + (r % w) + 1
+        v[:n] += np.exp(s[r, :n] - lse[r])
+    np.testing.assert_allclose(v, oracle.votes(q, keys, w), rtol=1e-12)
