@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="replay each step as a captured HIP graph (default) or launch eagerly")
     ap.add_argument("--two-pass", action="store_true", help="force the two-pass scoring path")
+    ap.add_argument("--lse", action="store_true",
+                    help="time snapkv_compress_lse: each window row's log-sum-exp given (as prefill attention "
+                         "would provide it), one read of K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -149,6 +153,25 @@ def main():
         n_sets += 1
     gen_threads = min(16, os.cpu_count() or 1)
 
+    def row_lse(q, K, cu):
+        """Each window row's log-sum-exp over the keys it sees, in fp32 with plain torch ops
+        (input preparation outside the timed region, standing in for prefill attention)."""
+        B, Hq, w, d = q.shape
+        G = Hq // K.shape[0]
+        out = torch.empty((B, Hq, w), dtype=torch.float32, device=q.device)
+        for r in range(B):
+            t0, t1 = int(cu[r]), int(cu[r + 1])
+            P = t1 - t0 - w
+            for h0 in range(0, Hq, G):
+                kf = K[h0 // G, t0:t1].float().contiguous()                       # [L, d]
+                qf = q[r, h0:h0 + G].float().reshape(G * w, d).contiguous()        # [G*w, d]
+                s = torch.matmul(qf, kf.t().contiguous()) / math.sqrt(d)          # [G*w, L]
+                i = torch.arange(G * w, device=q.device) % w
+                j = torch.arange(t1 - t0, device=q.device)
+                s = s.masked_fill(j[None, :] > (P + i)[:, None], float("-inf"))
+                out[r, h0:h0 + G] = torch.logsumexp(s, dim=1).reshape(G, w)
+        return out
+
     def to_dev(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -162,7 +185,8 @@ def main():
             q, K, V = to_dev(x["q_obs"]), to_dev(x["K"]), to_dev(x["V"])
             spec = _lib.make_spec(q, K, x["cu_seqlens"], wl.obs_window, wl.pool_kernel, wl.ratio, wl.budget,
                                   two_pass=args.two_pass)
-            layers.append(dict(q=q, K=K, V=V, spec=spec, cu=x["cu_seqlens"],
+            lse = row_lse(q, K, x["cu_seqlens"]) if args.lse else None
+            layers.append(dict(q=q, K=K, V=V, spec=spec, cu=x["cu_seqlens"], lse=lse,
                                host=x if (s == 0 and l == 0) else None))
         sets.append(layers)
     spec0 = sets[0][0]["spec"]
@@ -177,11 +201,19 @@ def main():
 
     def enqueue(layers):
         for ly in layers:
-            st = lib.snapkv_compress(ctypes.byref(ly["spec"].pb), ctypes.c_void_p(ly["q"].data_ptr()),
-                                     ctypes.c_void_p(ly["K"].data_ptr()), ctypes.c_void_p(ly["V"].data_ptr()),
-                                     ctypes.c_void_p(K_out.data_ptr()), ctypes.c_void_p(V_out.data_ptr()),
-                                     ctypes.c_void_p(idx.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()),
-                                     ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream))
+            if ly["lse"] is None:
+                st = lib.snapkv_compress(ctypes.byref(ly["spec"].pb), ctypes.c_void_p(ly["q"].data_ptr()),
+                                         ctypes.c_void_p(ly["K"].data_ptr()), ctypes.c_void_p(ly["V"].data_ptr()),
+                                         ctypes.c_void_p(K_out.data_ptr()), ctypes.c_void_p(V_out.data_ptr()),
+                                         ctypes.c_void_p(idx.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()),
+                                         ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream))
+            else:
+                st = lib.snapkv_compress_lse(ctypes.byref(ly["spec"].pb), ctypes.c_void_p(ly["q"].data_ptr()),
+                                             ctypes.c_void_p(ly["K"].data_ptr()), ctypes.c_void_p(ly["V"].data_ptr()),
+                                             ctypes.c_void_p(ly["lse"].data_ptr()),
+                                             ctypes.c_void_p(K_out.data_ptr()), ctypes.c_void_p(V_out.data_ptr()),
+                                             ctypes.c_void_p(idx.data_ptr()), None, ctypes.c_void_p(ws.data_ptr()),
+                                             ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream.cuda_stream))
             if st != 0:
                 raise RuntimeError("snapkv_compress: %s" % lib.snapkv_last_error().decode())
 
@@ -294,10 +326,18 @@ def main():
     gather_bytes = 4 * Hkv * spec0.sum_out * d * esz + Hkv * spec0.sum_k * 4
     path_bytes = Hkv * T * d * esz + q_bytes + 4 * Hkv * spec0.sum_out * d * esz  # K once, q once, rows r+w
 
-    obs_name = "obs_score_votes" if args.two_pass else "obs_score_fused"
+    # the scoring kernel that ran: fused, the LSE-fed votes pass, or (two-pass) the three launches
+    if args.lse:
+        obs_name = "obs_score_votes"
+    elif "obs_score_fused" in kernels_us:
+        obs_name = "obs_score_fused"
+    else:
+        obs_name = "obs_score_votes"
     obs_us = kernels_us.get(obs_name)
-    if args.two_pass and obs_us is not None:
+    roof_name = obs_name
+    if obs_name == "obs_score_votes" and not args.lse and obs_us is not None:
         obs_us = sum(kernels_us.get(k, 0.0) for k in ("obs_score_stats", "obs_stats_merge", "obs_score_votes"))
+        roof_name = "obs_score_stats+obs_stats_merge+obs_score_votes"
     obs_launches = launches_per_step.get(obs_name, 1.0) or 1.0
     obs_bytes_launch = obs_bytes * layers_per_step / obs_launches
     achieved = obs_bytes_launch / (obs_us * 1e-6) / 1e9 if obs_us else None
@@ -360,8 +400,8 @@ def main():
                    "layers_per_step": layers_per_step, "input_sets": n_sets,
                    "launch": "one graph of all timed steps" if launch == "graph" else launch,
                    "kernel_timing": "traced eager steps" + (" after the graph replays" if launch == "graph" else ""),
-                   "scoring": "two_pass" if args.two_pass else "fused"},
-        "roofline": {"kernel": obs_name, "bound": "hbm",
+                   "scoring": "lse_fed" if args.lse else ("two_pass" if obs_name != "obs_score_fused" else "fused")},
+        "roofline": {"kernel": roof_name, "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
                      "traffic": traffic, "alg_bytes_per_launch": int(obs_bytes_launch),

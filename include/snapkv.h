@@ -162,6 +162,24 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
                     void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * snapkv_scores_lse, snapkv_compress_lse -- the same outputs as snapkv_scores and
+ * snapkv_compress from a single read of K, for callers that already hold every window
+ * row's softmax normaliser (prefill attention computes it for these rows):
+ *   lse : float32 [B][H_q][L_obs], contiguous, 16-byte aligned: lse[r][h][i] =
+ *         ln sum_j exp(q . k_j / sqrt(d)) over exactly the keys row i sees under the
+ *         problem's variant (prefix plus window up to the row for SNAPKV_CAUSAL_WINDOW,
+ *         the prefix only for SNAPKV_PREFIX_ONLY); -infinity for a row that sees no key.
+ * The weights are exp(q . k_j / sqrt(d) - lse), so a wrong lse scales that row's
+ * weights instead of being detected.  Same conventions and errors as the calls above;
+ * SNAPKV_FLAG_TWO_PASS has no effect (there is no stats pass).
+ */
+int snapkv_scores_lse(const snapkv_problem *pb, const void *q_obs, const void *K, const float *lse, float *votes,
+                      float *pooled, void *ws, size_t ws_bytes, void *stream);
+int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, const float *lse,
+                        void *K_out, void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
  * Kernel trace (profiling hook).  While a trace is open on the calling thread,
  * the i-th kernel a snapkv_* call launches (i < n_pairs) carries events[2i] and
  * events[2i+1] as the start and stop events of its dispatch

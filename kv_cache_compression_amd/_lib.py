@@ -24,6 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
+           "snapkv_scores_lse", "snapkv_compress_lse",
            "snapkv_trace_begin", "snapkv_trace_end", "snapkv_kernel_name",
            "snapkv_strerror", "snapkv_last_error", "snapkv_version")
 
@@ -75,7 +76,10 @@ def load() -> ctypes.CDLL:
             lib.snapkv_select.argtypes = [P, vp, vp, vp, sz, vp]
             lib.snapkv_gather.argtypes = [P, vp, vp, vp, vp, vp, vp]
             lib.snapkv_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-            for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress"):
+            lib.snapkv_scores_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.snapkv_compress_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
+                      "snapkv_scores_lse", "snapkv_compress_lse"):
                 getattr(lib, f).restype = ctypes.c_int
             lib.snapkv_strerror.argtypes = [ctypes.c_int]
             lib.snapkv_strerror.restype = ctypes.c_char_p
@@ -191,18 +195,30 @@ def workspace(spec: Spec, device) -> torch.Tensor:
     return ws
 
 
+def _check_lse(lse, q_obs):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q_obs.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H_q, L_obs]")
+
+
 def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-           variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None):
-    """snapkv_scores: returns (votes or None, pooled), float32 [H_kv, sum_P]."""
+           variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None, lse=None):
+    """snapkv_scores (snapkv_scores_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs] is
+    given): returns (votes or None, pooled), float32 [H_kv, sum_P]."""
     spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
     dev = K.device
     votes = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev) if want_votes else None
     pooled = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev)
     if ws is None:
         ws = workspace(spec, dev)
-    st = load().snapkv_scores(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(votes), _ptr(pooled),
-                              _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
-    _check(st, "snapkv_scores")
+    if lse is None:
+        st = load().snapkv_scores(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(votes), _ptr(pooled),
+                                  _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+        _check(st, "snapkv_scores")
+    else:
+        _check_lse(lse, q_obs)
+        st = load().snapkv_scores_lse(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(lse), _ptr(votes),
+                                      _ptr(pooled), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+        _check(st, "snapkv_scores_lse")
     return votes, pooled
 
 
@@ -237,8 +253,9 @@ def gather(K, V, idx, q_obs, cu_seqlens=None, *, obs_window=32, pool_kernel=7, r
 
 
 def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-             variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None):
-    """snapkv_compress: the whole path.
+             variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None, lse=None):
+    """snapkv_compress (snapkv_compress_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs]
+    is given): the whole path.
 
     Returns dict(K_out, V_out [H_kv, sum_out, d], idx int32 [H_kv, sum_k], cu_out int64 [B+1], k int64 [B],
     pooled float32 [H_kv, sum_P] if want_pooled).  Defaults follow the pages' listing
@@ -257,9 +274,16 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
         K_out, V_out, idx, pooled = out["K_out"], out["V_out"], out["idx"], out.get("pooled")
     if ws is None:
         ws = workspace(spec, dev)
-    st = load().snapkv_compress(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(V), _ptr(K_out), _ptr(V_out),
-                                _ptr(idx), _ptr(pooled), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
-    _check(st, "snapkv_compress")
+    if lse is None:
+        st = load().snapkv_compress(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(V), _ptr(K_out), _ptr(V_out),
+                                    _ptr(idx), _ptr(pooled), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
+        _check(st, "snapkv_compress")
+    else:
+        _check_lse(lse, q_obs)
+        st = load().snapkv_compress_lse(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(V), _ptr(lse),
+                                        _ptr(K_out), _ptr(V_out), _ptr(idx), _ptr(pooled), _ptr(ws),
+                                        ctypes.c_size_t(ws.numel()), _stream())
+        _check(st, "snapkv_compress_lse")
     res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy())
     if pooled is not None:
         res["pooled"] = pooled

@@ -320,8 +320,8 @@ static bool fused_fits(const Plan &p, const Group &gr, int grid) {
 }
 
 // Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
-int run_scores(const Plan &p, const void *q, const void *K, float *votes, float *pooled, bool pool, char *ws,
-               hipStream_t stream) {
+int run_scores(const Plan &p, const void *q, const void *K, const float *lse, float *votes, float *pooled,
+               bool pool, char *ws, hipStream_t stream) {
     DevInfo di;
     int st = device_info(&di);
     if (st) return st;
@@ -363,6 +363,8 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         op.spin_limit = kSpinLimit;
         op.n_chunks = C;
         op.vplane = (int64_t)p.Hkv * p.sum_P;
+        op.lse = lse;
+        op.lse_scale = (float)sqrt((double)p.d);
         op.rt = gr.rt;
         const int64_t items = (int64_t)gr.n_slabs * C;
         const int grid = items < resident ? (int)items : resident;
@@ -371,7 +373,12 @@ int run_scores(const Plan &p, const void *q, const void *K, float *votes, float 
         const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && (int64_t)gr.max_ns * C <= resident &&
                            fused_fits(p, gr, grid);
         const int n_seg = gr.rt.n * p.Hkv;
-        if (fused) {
+        if (lse) {
+            // the caller's row stats: one read of K, no barrier
+            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, kVotes, keep), dim3((unsigned)items),
+                        dim3(cfg.threads()), &op, stream);
+            if (st) return st;
+        } else if (fused) {
             st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);
             if (st) return st;
         } else {
@@ -586,19 +593,30 @@ int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host,
     return SNAPKV_OK;
 }
 
-int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, float *votes, float *pooled,
-                  void *ws, size_t ws_bytes, void *stream) {
+static int scores_impl(const snapkv_problem *pb, const void *q_obs, const void *K, const float *lse, bool need_lse,
+                       float *votes, float *pooled, void *ws, size_t ws_bytes, void *stream) {
     Plan p;
     int st = make_plan(pb, &p);
     if (!st) st = check_ptr(q_obs, "q_obs");
     if (!st) st = check_ptr(K, "K");
+    if (!st && need_lse) st = check_ptr(lse, "lse");
     if (!st) st = check_opt_ptr(votes, "votes");
     if (!st) st = check_ptr(pooled, "pooled");
     if (!st) st = check_ws(p, ws, ws_bytes);
     if (st) return st;
     char *w = (char *)ws;
     float *v = votes ? votes : (float *)(w + p.off_votes);
-    return finish(run_scores(p, q_obs, K, v, pooled, true, w, (hipStream_t)stream));
+    return finish(run_scores(p, q_obs, K, lse, v, pooled, true, w, (hipStream_t)stream));
+}
+
+int snapkv_scores(const snapkv_problem *pb, const void *q_obs, const void *K, float *votes, float *pooled,
+                  void *ws, size_t ws_bytes, void *stream) {
+    return scores_impl(pb, q_obs, K, nullptr, false, votes, pooled, ws, ws_bytes, stream);
+}
+
+int snapkv_scores_lse(const snapkv_problem *pb, const void *q_obs, const void *K, const float *lse, float *votes,
+                      float *pooled, void *ws, size_t ws_bytes, void *stream) {
+    return scores_impl(pb, q_obs, K, lse, true, votes, pooled, ws, ws_bytes, stream);
 }
 
 int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, void *ws, size_t ws_bytes,
@@ -631,13 +649,15 @@ int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const 
     return finish(run_gather(p, K, V, idx, K_out, V_out, (hipStream_t)stream));
 }
 
-int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
-                    void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream) {
+static int compress_impl(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, const float *lse,
+                         bool need_lse, void *K_out, void *V_out, int32_t *idx, float *pooled, void *ws,
+                         size_t ws_bytes, void *stream) {
     Plan p;
     int st = make_plan(pb, &p);
     if (!st) st = check_ptr(q_obs, "q_obs");
     if (!st) st = check_ptr(K, "K");
     if (!st) st = check_ptr(V, "V");
+    if (!st && need_lse) st = check_ptr(lse, "lse");
     if (!st) st = check_ptr(K_out, "K_out");
     if (!st) st = check_ptr(V_out, "V_out");
     if (!st) st = check_opt_ptr(idx, "idx");
@@ -651,10 +671,21 @@ int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, 
     const bool need_pooled = p.max_P > select_lds_positions() || !select_fuses_pool(p, p.max_P);
     float *pl = pooled ? pooled : (need_pooled ? (float *)(w + p.off_pooled) : nullptr);
     int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
-    st = run_scores(p, q_obs, K, votes, nullptr, false, w, s);
+    st = run_scores(p, q_obs, K, lse, votes, nullptr, false, w, s);
     if (!st) st = run_select(p, votes, pl, ix, w, s);
     if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s);
     return finish(st);
+}
+
+int snapkv_compress(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
+                    void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes, void *stream) {
+    return compress_impl(pb, q_obs, K, V, nullptr, false, K_out, V_out, idx, pooled, ws, ws_bytes, stream);
+}
+
+int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, const float *lse,
+                        void *K_out, void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes,
+                        void *stream) {
+    return compress_impl(pb, q_obs, K, V, lse, true, K_out, V_out, idx, pooled, ws, ws_bytes, stream);
 }
 
 int snapkv_trace_begin(void *const *events, int n_pairs) {

@@ -462,11 +462,22 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
         if constexpr (MODE == kVotes) {
             if (tid < MROWS) {
                 const int row = tid;
-                float2 mg = make_float2(0.f, 0.f);
-                if (row < Mc) mg = p.merged[(int64_t)seg * p.M_pad + row];
-                const bool ok = row < Mc && mg.x != neg_inf() && mg.y > 0.f;
-                sh_rowm[row] = ok ? mg.x : 0.f;
-                sh_f[row] = ok ? 1.f / mg.y : 0.f;
+                if (p.lse) {
+                    // caller's log-sum-exp: weight = exp(s / sqrt(d) - lse) = exp2(s * c - lse * log2(e)),
+                    // i.e. row max lse * sqrt(d) and row sum 1
+                    float lv = neg_inf();
+                    if (row < Mc)
+                        lv = p.lse[((int64_t)p.rt.qi[sp.r] * p.Hq + (int64_t)sp.g * p.G) * p.w + cbase + row];
+                    const bool ok = lv != neg_inf();
+                    sh_rowm[row] = ok ? lv * p.lse_scale : 0.f;
+                    sh_f[row] = ok ? 1.f : 0.f;
+                } else {
+                    float2 mg = make_float2(0.f, 0.f);
+                    if (row < Mc) mg = p.merged[(int64_t)seg * p.M_pad + row];
+                    const bool ok = row < Mc && mg.x != neg_inf() && mg.y > 0.f;
+                    sh_rowm[row] = ok ? mg.x : 0.f;
+                    sh_f[row] = ok ? 1.f / mg.y : 0.f;
+                }
             }
             __syncthreads();
             static_for<RTW>([&](auto rt) {

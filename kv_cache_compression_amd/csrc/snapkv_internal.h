@@ -62,6 +62,8 @@ struct ObsParams {
     uint32_t spin_limit;        // polls before a barrier wait gives up
     int32_t n_chunks;           // row chunks of kChunkRows query rows per KV head
     int64_t vplane;             // floats between the votes planes of consecutive chunks
+    const float *lse;           // kVotes: caller's row log-sum-exp [B][H_q][L_obs] instead of merged
+    float lse_scale;            // sqrt(d): lse * lse_scale * c = lse * log2(e)
     ReqTable rt;
 };
 

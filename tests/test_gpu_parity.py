@@ -156,6 +156,52 @@ def test_select_exact_on_crafted_votes(levels):
                                               err_msg="P=%d k=%d g=%d %s" % (P, k, g, kw))
 
 
+LSE_CASES = [
+    # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, variant
+    ("lse_mha_bf16_d128", [3000, 1200], 4, 4, 128, "bf16", 32, 7, 0.05, None, 0),
+    ("lse_gqa_chunks", [2600], 16, 2, 64, "bf16", 16, 5, 0.05, None, 0),
+    ("lse_prefix_only", [2100, 64], 8, 2, 128, "bf16", 32, 7, 0.1, None, 1),
+    ("lse_f32_d64", [1500], 4, 2, 64, "f32", 32, 7, None, 90, 0),
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=[c[0] for c in LSE_CASES])
+def test_lse_fed_single_pass(case):
+    """snapkv_scores_lse / snapkv_compress_lse with each row's log-sum-exp from the oracle
+    (rounded to float32) give the oracle's votes, pooled votes, selection and gather."""
+    name, lengths, Hq, Hkv, d, dt, w, kp, ratio, budget, variant = case
+    snap = _snap()
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget,
+                      n_plant=8, name=name)
+    _say("case %s" % name)
+    x = synth.make_inputs(wl)
+    cu = x["cu_seqlens"]
+    lse_ref = oracle.lse_all(x["q_obs"], x["K"], cu, w, variant)
+    lse = torch.from_numpy(lse_ref.astype(np.float32)).cuda()
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, variant=variant)
+    votes, pooled = snap.scores(q, K, cu, lse=lse, **kw)
+    res = snap.compress(q, K, V, cu, lse=lse, want_pooled=True, **kw)
+    torch.cuda.synchronize()
+    spec = snap.make_spec(q, K, cu, w, kp, ratio, budget, variant)
+    ref = oracle.compress(x["q_obs"], x["K"], x["V"], cu, w, kp, ratio=ratio, budget=budget, variant=variant,
+                          with_gather=False)
+    votes, pooled_c = votes.cpu().numpy(), res["pooled"].cpu().numpy()
+    idx = res["idx"].cpu().numpy()
+    K_out = to_numpy_bits(res["K_out"])
+    for (r, g), rr in sorted(ref.items()):
+        t0, t1 = int(cu[r]), int(cu[r + 1])
+        P, k = t1 - t0 - w, rr["k"]
+        tag = "%s r=%d g=%d" % (name, r, g)
+        cols = slice(int(spec.cu_pfx[r]), int(spec.cu_pfx[r + 1]))
+        check_scores(votes[g, cols], rr["votes"], tag + " votes")
+        check_scores(pooled_c[g, cols], rr["pooled"], tag + " pooled")
+        ig = idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])]
+        check_selection(ig, rr["pooled"], rr["idx"], k, tag + " select")
+        check_select_exact(ig, pooled_c[g, cols], k, tag + " select-exact")
+        check_gather(x["K"][g, t0:t1], K_out[g, int(spec.cu_out[r]):int(spec.cu_out[r + 1])], ig, P, w, tag + " gather")
+
+
 def test_prefix_only_variant():
     wl = synth.custom([3000, 1500], 8, 2, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8,
                       name="prefix_only")
