@@ -50,6 +50,8 @@ def parse():
                          "would provide it), one read of K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--hit-rate", action="store_true",
+                    help="also time snapkv_hit_rate on the last step's selection (random attention, theta 0.05)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) and exit: the known-size "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings to bytes")
@@ -359,6 +361,30 @@ def main():
     if not (torch.equal(ref_idx, idx) and torch.equal(ref_k, K_out)):
         raise RuntimeError("timed outputs differ from an eager run of the same input")
 
+    # ---- Hit Rate kernel (optional): reads the attention and the selection once -----------
+    hit = None
+    if args.hit_rate:
+        a_cur = torch.rand((Hkv, spec0.sum_P), device=dev) * 0.1
+        counts = torch.empty((wl.batch, Hkv, 2), dtype=torch.int32, device=dev)
+        n_hit = 20
+        ev_h = [hip.events(2) for _ in range(n_hit)]
+        with torch.cuda.stream(stream):
+            for i in range(n_hit + 3):
+                if i >= 3:
+                    lib.snapkv_trace_begin(ctypes.cast(ev_h[i - 3], ctypes.POINTER(ctypes.c_void_p)), 1)
+                st = lib.snapkv_hit_rate(ctypes.byref(spec0.pb), ctypes.c_void_p(a_cur.data_ptr()),
+                                         ctypes.c_void_p(idx.data_ptr()), ctypes.c_double(0.05),
+                                         ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                if i >= 3:
+                    ids1 = (ctypes.c_int32 * 1)()
+                    lib.snapkv_trace_end(ids1, 1)
+                if st != 0:
+                    raise RuntimeError("snapkv_hit_rate: %s" % lib.snapkv_last_error().decode())
+        torch.cuda.synchronize()
+        us = 1e3 * sum(hip.elapsed_ms(ev_h[i][0], ev_h[i][1]) for i in range(n_hit)) / n_hit
+        hb = 4 * Hkv * spec0.sum_P + 4 * Hkv * spec0.sum_k + 8 * wl.batch * Hkv
+        hit = {"avg_launch_us": round(us, 3), "alg_bytes": hb, "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
+
     # ---- CPU baseline: the oracle on the host cores --------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -411,6 +437,8 @@ def main():
         "kernels_us": kernels_us,
         "cpu_baseline": cpu,
     }
+    if hit is not None:
+        out["hit_rate_kernel"] = hit
     print(json.dumps(out), flush=True)
 
 

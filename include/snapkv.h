@@ -180,6 +180,22 @@ int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void 
                         void *stream);
 
 /*
+ * snapkv_hit_rate -- the Hit Rate of a selection (section Hit Rate（適中率）の定式化):
+ * for each (request, KV head), `above` = the prefix positions whose attention in the
+ * current generation step exceeds theta (strictly), and `hits` = those among them that
+ * the selection kept.  The rate is hits / above (undefined, NaN, when above = 0); sums of
+ * the counts give the rate over several heads or requests.
+ *   a_cur  : float32 [H_kv][sum_P] (the votes layout), attention to each prefix position.
+ *   idx    : int32 [H_kv][sum_k], strictly ascending per (request, KV head), as
+ *            snapkv_select writes it.
+ *   theta  : threshold (the page uses 0.05); compared in double against each value.
+ *   counts : out, uint32 [B][H_kv][2] = (hits, above).
+ * No workspace.  Errors as for the other calls (theta NaN -> SNAPKV_EINVAL).
+ */
+int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t *idx, double theta, uint32_t *counts,
+                    void *stream);
+
+/*
  * Kernel trace (profiling hook).  While a trace is open on the calling thread,
  * the i-th kernel a snapkv_* call launches (i < n_pairs) carries events[2i] and
  * events[2i+1] as the start and stop events of its dispatch
@@ -201,7 +217,8 @@ typedef enum {
     SNAPKV_K_SELECT = 6,      /* topk_select */
     SNAPKV_K_GATHER = 7,      /* kv_gather */
     SNAPKV_K_SUM_CHUNKS = 8,  /* sum of the votes of the row chunks (G * L_obs > 32) */
-    SNAPKV_K_SELECT_TILES = 9 /* topk_select of segments longer than 32768 positions (4 phases) */
+    SNAPKV_K_SELECT_TILES = 9, /* topk_select of segments longer than 32768 positions (4 phases) */
+    SNAPKV_K_HIT_RATE = 10     /* snapkv_hit_rate */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

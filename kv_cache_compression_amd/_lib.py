@@ -24,7 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-           "snapkv_scores_lse", "snapkv_compress_lse",
+           "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate",
            "snapkv_trace_begin", "snapkv_trace_end", "snapkv_kernel_name",
            "snapkv_strerror", "snapkv_last_error", "snapkv_version")
 
@@ -78,8 +78,9 @@ def load() -> ctypes.CDLL:
             lib.snapkv_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_scores_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_compress_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.snapkv_hit_rate.argtypes = [P, vp, vp, ctypes.c_double, vp, vp]
             for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-                      "snapkv_scores_lse", "snapkv_compress_lse"):
+                      "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate"):
                 getattr(lib, f).restype = ctypes.c_int
             lib.snapkv_strerror.argtypes = [ctypes.c_int]
             lib.snapkv_strerror.restype = ctypes.c_char_p
@@ -288,3 +289,18 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
     if pooled is not None:
         res["pooled"] = pooled
     return res
+
+
+def hit_rate_counts(a_cur, idx, q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
+                    theta=0.05):
+    """snapkv_hit_rate: uint32 [B, H_kv, 2] = (hits, above) per (request, KV head)."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget)
+    if a_cur.dtype != torch.float32 or tuple(a_cur.shape) != (spec.Hkv, spec.sum_P) or not a_cur.is_contiguous():
+        raise ValueError("a_cur must be contiguous float32 [H_kv, sum_P]")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (spec.Hkv, spec.sum_k) or not idx.is_contiguous():
+        raise ValueError("idx must be contiguous int32 [H_kv, sum_k]")
+    counts = torch.empty((spec.pb.batch, spec.Hkv, 2), dtype=torch.int32, device=K.device)
+    st = load().snapkv_hit_rate(ctypes.byref(spec.pb), _ptr(a_cur), _ptr(idx), ctypes.c_double(theta), _ptr(counts),
+                                _stream())
+    _check(st, "snapkv_hit_rate")
+    return counts

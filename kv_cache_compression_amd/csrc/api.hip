@@ -688,6 +688,37 @@ int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void 
     return compress_impl(pb, q_obs, K, V, lse, true, K_out, V_out, idx, pooled, ws, ws_bytes, stream);
 }
 
+int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t *idx, double theta, uint32_t *counts,
+                    void *stream) {
+    Plan p;
+    int st = make_plan(pb, &p);
+    if (!st) st = check_ptr(a_cur, "a_cur");
+    if (!st) st = check_ptr(idx, "idx");
+    if (!st) st = check_ptr(counts, "counts");
+    if (!st && !(theta == theta)) st = fail(SNAPKV_EINVAL, "theta is NaN");
+    if (st) return st;
+    DevInfo di;
+    st = device_info(&di);
+    if (st) return st;
+    for (const Group &gr : p.groups) {
+        HitParams hp;
+        memset(&hp, 0, sizeof hp);
+        hp.a_cur = a_cur;
+        hp.idx = idx;
+        hp.counts = counts;
+        hp.theta = theta;
+        hp.sum_P = p.sum_P;
+        hp.sum_k = p.sum_k;
+        hp.w = p.w;
+        hp.Hkv = p.Hkv;
+        hp.rt = gr.rt;
+        st = launch(SNAPKV_K_HIT_RATE, hit_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &hp,
+                    (hipStream_t)stream);
+        if (st) return finish(st);
+    }
+    return finish(SNAPKV_OK);
+}
+
 int snapkv_trace_begin(void *const *events, int n_pairs) {
     g_last_error.clear();
     if (!events || n_pairs < 1) return fail(SNAPKV_EINVAL, "trace needs events and n_pairs >= 1");
@@ -719,6 +750,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_GATHER: return "kv_gather";
         case SNAPKV_K_SUM_CHUNKS: return "sum_chunks";
         case SNAPKV_K_SELECT_TILES: return "topk_select_tiles";
+        case SNAPKV_K_HIT_RATE: return "hit_rate";
         default: return "unknown";
     }
 }

@@ -636,6 +636,82 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(const SelectPa
 }
 const void *select_kernel() { return (const void *)&topk_select_kernel; }
 
+// ---- hit rate -----------------------------------------------------------------------------------
+// One 1024-thread workgroup per (request, KV head).  The kept positions of up to kHitSpan
+// positions at a time (a contiguous run of the ascending idx, found by binary search) are
+// marked in an LDS bitmap with one coalesced pass over idx; then the attention values of the
+// span stream through with 16 loads in flight per thread.  The threshold test runs in fp64
+// on the fp32 attention values.
+constexpr int kHitSpan = 1 << 20;
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__global__ void __launch_bounds__(kSelThreads) hit_rate_kernel(const HitParams p) {
+    __shared__ uint32_t bits[kHitSpan / 32];
+    __shared__ int range[2];
+    __shared__ uint32_t wsum[2][kSelWaves];
+    const int seg = blockIdx.x;
+    const int r = seg / p.Hkv, g = seg - (seg / p.Hkv) * p.Hkv;
+    const int P = p.rt.L[r] - p.w;
+    const int k = p.rt.k[r];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *a = p.a_cur + (int64_t)g * p.sum_P + p.rt.pfx0[r];
+    const int32_t *ix = p.idx + (int64_t)g * p.sum_k + p.rt.k0[r];
+    uint32_t hits = 0, above = 0;
+    for (int c0 = 0; c0 < P; c0 += kHitSpan) {
+        const int span = P - c0 < kHitSpan ? P - c0 : kHitSpan;
+        for (int i = tid; i < (span + 31) / 32; i += kSelThreads) bits[i] = 0;
+        if (tid < 2) range[tid] = c0 == 0 && P <= kHitSpan ? (tid ? k : 0) : lower_bound_i32(ix, k, c0 + tid * kHitSpan);
+        __syncthreads();
+        for (int t = range[0] + tid; t < range[1]; t += kSelThreads) {
+            const int j = ix[t] - c0;  // in [0, span) for an ascending idx
+            if (j >= 0 && j < span) atomicOr(&bits[j >> 5], 1u << (j & 31));
+        }
+        __syncthreads();
+        for (int b0 = 0; b0 < span; b0 += 16 * kSelThreads) {
+            float v[16];
+            static_for<16>([&](auto i) {
+                const int jl = b0 + i() * kSelThreads + tid;
+                v[i()] = jl < span ? a[c0 + jl] : 0.f;
+            });
+            static_for<16>([&](auto i) {
+                const int jl = b0 + i() * kSelThreads + tid;
+                if (jl < span && (double)v[i()] > p.theta) {
+                    ++above;
+                    hits += (bits[jl >> 5] >> (jl & 31)) & 1u;
+                }
+            });
+        }
+        __syncthreads();
+    }
+    // workgroup sums (exact integers)
+    hits = wave_incl_scan(hits);
+    above = wave_incl_scan(above);
+    if (lane == 63) {
+        wsum[0][wave] = hits;
+        wsum[1][wave] = above;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t h = 0, n = 0;
+        for (int w2 = 0; w2 < kSelWaves; ++w2) {
+            h += wsum[0][w2];
+            n += wsum[1][w2];
+        }
+        p.counts[((int64_t)p.rt.qi[r] * p.Hkv + g) * 2 + 0] = h;
+        p.counts[((int64_t)p.rt.qi[r] * p.Hkv + g) * 2 + 1] = n;
+    }
+}
+const void *hit_kernel() { return (const void *)&hit_rate_kernel; }
+
 // ---- gather -----------------------------------------------------------------------------------
 // grid: (row tiles, KV heads).  An output row is row_bytes / 16 lanes of 16-byte copies; a
 // block pass covers 256 / lanes-per-row rows and each thread takes kGatherRows rows of a

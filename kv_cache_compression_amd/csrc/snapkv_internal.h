@@ -148,6 +148,17 @@ struct LongParams {
 const void *long_kernel();
 int select_tile_positions();
 
+struct HitParams {
+    const float *a_cur;         // [H_kv][sum_P]
+    const int32_t *idx;         // [H_kv][sum_k], ascending per segment
+    uint32_t *counts;           // [B][H_kv][2]: (kept and above theta, above theta)
+    double theta;
+    int64_t sum_P, sum_k;
+    int32_t w, Hkv;
+    ReqTable rt;
+};
+const void *hit_kernel();
+
 struct GatherParams {
     const void *K, *V;
     const int32_t *idx;

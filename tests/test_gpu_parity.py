@@ -202,6 +202,72 @@ def test_lse_fed_single_pass(case):
         check_gather(x["K"][g, t0:t1], K_out[g, int(spec.cu_out[r]):int(spec.cu_out[r + 1])], ig, P, w, tag + " gather")
 
 
+@pytest.mark.parametrize("lengths", [[3000, 40, 1200], [70000]], ids=["short", "long"])
+def test_hit_rate_matches_oracle(lengths):
+    """snapkv_hit_rate counts per (request, KV head) give the oracle's Hit Rate exactly: random
+    attention with values exactly at theta (as float32) and next to it, and a selection from
+    the compression path itself."""
+    snap = _snap()
+    w, Hkv = 32, 2
+    wl = synth.custom(lengths, 4, Hkv, 64, obs_window=w, pool_kernel=7, ratio=0.05, n_plant=4, name="hit")
+    x = synth.make_inputs(wl)
+    cu = x["cu_seqlens"]
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    res = snap.compress(q, K, V, cu, obs_window=w, pool_kernel=7, ratio=0.05)
+    spec = snap.make_spec(q, K, cu, w, 7, 0.05, None)
+    rng = np.random.default_rng(11)
+    a = (rng.random((Hkv, spec.sum_P)) * 0.1).astype(np.float32)
+    theta = 0.05
+    t32 = np.float32(theta)
+    a.ravel()[rng.integers(0, a.size, 500)] = t32                       # exactly theta in float32
+    a.ravel()[rng.integers(0, a.size, 500)] = np.nextafter(t32, np.float32(1))
+    a.ravel()[rng.integers(0, a.size, 500)] = np.nextafter(t32, np.float32(0))
+    counts = snap.hit_rate_counts(torch.from_numpy(a).cuda(), res["idx"], q, K, cu, obs_window=w, pool_kernel=7,
+                                  ratio=0.05, theta=theta)
+    torch.cuda.synchronize()
+    counts = counts.cpu().numpy().view(np.uint32)
+    idx = res["idx"].cpu().numpy()
+    for r in range(len(lengths)):
+        P = lengths[r] - w
+        for g in range(Hkv):
+            seg = a[g, int(spec.cu_pfx[r]):int(spec.cu_pfx[r + 1])]
+            mask = np.zeros(P, np.uint8)
+            mask[idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])]] = 1
+            ref = oracle.hit_rate(seg, mask, theta)
+            hits, above = int(counts[r, g, 0]), int(counts[r, g, 1])
+            assert above == int(np.sum(seg.astype(np.float64) > theta)), (r, g)
+            if above == 0:
+                assert np.isnan(ref)
+            else:
+                assert hits / above == ref, (r, g, hits, above, ref)
+
+
+def test_hit_rate_beyond_one_bitmap_span():
+    """A segment of more than 2^20 positions is counted span by span (a kept position
+    near every span edge)."""
+    snap = _snap()
+    w, Hkv, P = 8, 1, (1 << 20) + 5000
+    cu = np.array([0, P + w], np.int32)
+    q = torch.zeros((1, 1, w, 64), dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros((Hkv, P + w, 64), dtype=torch.bfloat16, device="cuda")
+    spec = snap.make_spec(q, K, cu, w, 7, None, 4000)
+    rng = np.random.default_rng(12)
+    keep = np.sort(np.concatenate([rng.choice(P, 3990, replace=False),
+                                   [(1 << 20) - 2, (1 << 20) - 1, 1 << 20, (1 << 20) + 1, 0, P - 1]]))
+    keep = np.unique(keep)[:4000]
+    keep = np.sort(np.concatenate([keep, np.setdiff1d(np.arange(P), keep)[:4000 - keep.size]]))
+    idx = torch.from_numpy(keep.astype(np.int32)[None, :]).cuda()
+    a = (rng.random((Hkv, P)) * 0.1).astype(np.float32)
+    counts = snap.hit_rate_counts(torch.from_numpy(a).cuda(), idx, q, K, cu, obs_window=w, pool_kernel=7,
+                                  budget=4000, theta=0.05)
+    torch.cuda.synchronize()
+    hits, above = (int(v) for v in counts.cpu().numpy().view(np.uint32)[0, 0])
+    mask = np.zeros(P, np.uint8)
+    mask[keep] = 1
+    assert above == int(np.sum(a[0].astype(np.float64) > 0.05))
+    assert hits / above == oracle.hit_rate(a[0], mask, 0.05)
+
+
 def test_prefix_only_variant():
     wl = synth.custom([3000, 1500], 8, 2, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8,
                       name="prefix_only")
