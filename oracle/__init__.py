@@ -12,6 +12,8 @@ from .ref import (  # noqa: F401
     votes,
     row_lse,
     lse_all,
+    decode,
+    decode_all,
     pool,
     k_of,
     select,

@@ -69,6 +69,8 @@ def _load():
             lib.snapkv_oracle_votes.restype = None
             lib.snapkv_oracle_row_lse.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i64, i64, i32, vp, vp]
             lib.snapkv_oracle_row_lse.restype = None
+            lib.snapkv_oracle_decode.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, i64, i64, vp, vp]
+            lib.snapkv_oracle_decode.restype = None
             lib.snapkv_oracle_pool.argtypes = [vp, i64, i32, vp]
             lib.snapkv_oracle_pool.restype = None
             lib.snapkv_oracle_k.argtypes = [i64, i32, dbl, i64]
@@ -145,6 +147,36 @@ def lse_all(q_obs: np.ndarray, K: np.ndarray, cu_seqlens, w: int, variant: int =
         t0, t1 = int(cu_seqlens[r]), int(cu_seqlens[r + 1])
         for h in range(Hq):
             out[r, h] = row_lse(q_obs[r, h], K[h // G, t0:t1], w, variant)
+    return out
+
+
+def decode(q: np.ndarray, keys: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """Decode attention of G query rows q [G, d] over cached rows keys/values [n, d]
+    (same dtype): softmax(q k^T / sqrt(d)) v in fp64, [G, d]; zeros when n = 0."""
+    q = np.ascontiguousarray(q)
+    keys = np.ascontiguousarray(keys)
+    values = np.ascontiguousarray(values)
+    dt = _dtype_code(q)
+    assert _dtype_code(keys) == dt == _dtype_code(values) and keys.shape == values.shape
+    G, d = q.shape
+    n = keys.shape[0]
+    out = np.empty((G, d), np.float64)
+    row_buf = np.empty(max(n, 1), np.float64)
+    _load().snapkv_oracle_decode(_ptr(q), dt, G, d, _ptr(keys), _ptr(values), d, n, _ptr(out), _ptr(row_buf))
+    return out
+
+
+def decode_all(q: np.ndarray, K: np.ndarray, V: np.ndarray, cu_rows) -> np.ndarray:
+    """decode() for every request and KV head: q [B, H_q, d], K/V [H_kv, T, d] with request r
+    owning rows cu_rows[r] .. cu_rows[r+1]-1; returns fp64 [B, H_q, d]."""
+    B, Hq, d = q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, d), np.float64)
+    for r in range(B):
+        a, b = int(cu_rows[r]), int(cu_rows[r + 1])
+        for g in range(Hkv):
+            out[r, g * G:(g + 1) * G] = decode(q[r, g * G:(g + 1) * G], K[g, a:b], V[g, a:b])
     return out
 
 

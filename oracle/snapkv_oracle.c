@@ -257,6 +257,40 @@ static void run_job(snapkv_oracle_job *jb)
     free(scratch);
 }
 
+/*
+ * Decode attention over a (compressed) cache: the step after the compression (page
+ * "論文解説: SnapKV ..." section デコード速度とメモリ効率, and the KV-cache chapter's decode
+ * step, where one new query attends to every cached key).  For G query rows q[G][d] of
+ * one KV head and n_rows cached rows: out[h] = sum_j softmax_j(q_h . k_j / sqrt(d)) v_j,
+ * in fp64.  out is zero when n_rows = 0.
+ */
+void snapkv_oracle_decode(const void *q, int dtype, int32_t G, int32_t d, const void *keys, const void *values,
+                          int64_t row_stride, int64_t n_rows, double *out, double *row_buf)
+{
+    double scale = 1.0 / sqrt((double)d);
+    for (int32_t h = 0; h < G; ++h) {
+        double *o = out + (int64_t)h * d;
+        for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+        if (n_rows <= 0) continue;
+        const void *qh = row_ptr(q, dtype, h, d);
+        for (int64_t j = 0; j < n_rows; ++j) {
+            const void *kj = row_ptr(keys, dtype, j, row_stride);
+            double s = 0.0;
+            for (int32_t c = 0; c < d; ++c) s += widen(qh, dtype, c) * widen(kj, dtype, c);
+            row_buf[j] = s * scale;
+        }
+        double m = row_buf[0];
+        for (int64_t j = 1; j < n_rows; ++j) if (row_buf[j] > m) m = row_buf[j];
+        double l = 0.0;
+        for (int64_t j = 0; j < n_rows; ++j) l += exp(row_buf[j] - m);
+        for (int64_t j = 0; j < n_rows; ++j) {
+            const void *vj = row_ptr(values, dtype, j, row_stride);
+            double p = exp(row_buf[j] - m) / l;
+            for (int32_t c = 0; c < d; ++c) o[c] += p * widen(vj, dtype, c);
+        }
+    }
+}
+
 /* Run independent jobs, one OpenMP thread per job at a time.  Returns the thread count used. */
 int snapkv_oracle_run_jobs(snapkv_oracle_job *jobs, int64_t n_jobs, int n_threads)
 {

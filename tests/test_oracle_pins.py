@@ -361,3 +361,38 @@ def test_row_lse_normalises_the_votes():
         n = P + (r % w) + 1
         v[:n] += np.exp(s[r, :n] - lse[r])
     np.testing.assert_allclose(v, oracle.votes(q, keys, w), rtol=1e-12)
+
+
+# ---- decode attention over the compressed cache -----------------------------------------------
+
+def test_decode_uniform_scores_give_the_mean_value():
+    """q = 0: every score is 0, so the output is the mean of the cached value rows."""
+    rng = np.random.default_rng(20)
+    n, d = 37, 16
+    q = np.zeros((3, d), np.float32)
+    k = rng.standard_normal((n, d)).astype(np.float32)
+    v = rng.standard_normal((n, d)).astype(np.float32)
+    np.testing.assert_allclose(oracle.decode(q, k, v), np.tile(v.astype(np.float64).mean(0), (3, 1)), rtol=1e-13)
+
+
+def test_decode_single_row_and_empty_cache():
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((2, 8)).astype(np.float32)
+    k = rng.standard_normal((1, 8)).astype(np.float32)
+    v = rng.standard_normal((1, 8)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.decode(q, k, v), np.tile(v.astype(np.float64), (2, 1)))
+    assert not oracle.decode(q, k[:0], v[:0]).any()
+
+
+def test_decode_matches_torch_sdpa_float64():
+    """Against torch's scaled_dot_product_attention on the CPU in float64 (bf16 inputs)."""
+    import torch
+    from kv_cache_compression_amd import synth
+    rng = np.random.default_rng(22)
+    G, n, d = 4, 300, 64
+    q = synth.round_bf16((2 * rng.standard_normal((G, d))).astype(np.float32))
+    k = synth.round_bf16(rng.standard_normal((n, d)).astype(np.float32))
+    v = synth.round_bf16(rng.standard_normal((n, d)).astype(np.float32))
+    f64 = lambda a: torch.from_numpy(synth.bf16_to_f32(a).astype(np.float64))
+    ref = torch.nn.functional.scaled_dot_product_attention(f64(q)[None, None], f64(k)[None, None], f64(v)[None, None])
+    np.testing.assert_allclose(oracle.decode(q, k, v), ref[0, 0].numpy(), rtol=1e-12, atol=1e-14)
