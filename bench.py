@@ -50,6 +50,8 @@ def parse():
                          "would provide it), one read of K")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--decode", action="store_true",
+                    help="also time snapkv_decode: one query row per head over the last step's compressed cache")
     ap.add_argument("--hit-rate", action="store_true",
                     help="also time snapkv_hit_rate on the last step's selection (random attention, theta 0.05)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -385,6 +387,44 @@ def main():
         hb = 4 * Hkv * spec0.sum_P + 4 * Hkv * spec0.sum_k + 8 * wl.batch * Hkv
         hit = {"avg_launch_us": round(us, 3), "alg_bytes": hb, "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
 
+    # ---- decode attention over the compressed cache (optional) ------------------------------
+    dec = None
+    if args.decode:
+        qd = torch.randn((wl.batch, wl.num_q_heads, d), device=dev).to(K_out.dtype)
+        cu_rows = np.ascontiguousarray(spec0.cu_out.astype(np.int64))
+        dprob = _lib.DecodeProblem()
+        dprob.batch, dprob.num_q_heads, dprob.num_kv_heads, dprob.head_dim = wl.batch, wl.num_q_heads, Hkv, d
+        dprob.dtype = 1 if wl.dtype == "bf16" else 0
+        dprob.kv_head_stride, dprob.kv_token_stride = K_out.stride(0), K_out.stride(1)
+        dprob.cu_rows_host = cu_rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        need = ctypes.c_size_t()
+        if lib.snapkv_decode_plan(ctypes.byref(dprob), ctypes.byref(need)) != 0:
+            raise RuntimeError("snapkv_decode_plan: %s" % lib.snapkv_last_error().decode())
+        dws = torch.empty(max(need.value, 256), dtype=torch.uint8, device=dev)
+        dout = torch.empty((wl.batch, wl.num_q_heads, d), dtype=torch.float32, device=dev)
+        n_dec = 20
+        ev_d = [hip.events(4) for _ in range(n_dec)]
+        with torch.cuda.stream(stream):
+            for i in range(n_dec + 3):
+                if i >= 3:
+                    lib.snapkv_trace_begin(ctypes.cast(ev_d[i - 3], ctypes.POINTER(ctypes.c_void_p)), 2)
+                st = lib.snapkv_decode(ctypes.byref(dprob), ctypes.c_void_p(qd.data_ptr()),
+                                       ctypes.c_void_p(K_out.data_ptr()), ctypes.c_void_p(V_out.data_ptr()),
+                                       ctypes.c_void_p(dout.data_ptr()), ctypes.c_void_p(dws.data_ptr()),
+                                       ctypes.c_size_t(dws.numel()), ctypes.c_void_p(stream.cuda_stream))
+                if i >= 3:
+                    ids2 = (ctypes.c_int32 * 2)()
+                    lib.snapkv_trace_end(ids2, 2)
+                if st != 0:
+                    raise RuntimeError("snapkv_decode: %s" % lib.snapkv_last_error().decode())
+        torch.cuda.synchronize()
+        part_us = 1e3 * sum(hip.elapsed_ms(ev_d[i][0], ev_d[i][1]) for i in range(n_dec)) / n_dec
+        comb_us = 1e3 * sum(hip.elapsed_ms(ev_d[i][2], ev_d[i][3]) for i in range(n_dec)) / n_dec
+        db = 2 * Hkv * spec0.sum_out * d * esz + 2 * wl.batch * wl.num_q_heads * d * (esz + 4)
+        dec = {"decode_attention_us": round(part_us, 3), "decode_combine_us": round(comb_us, 3),
+               "cache_rows_per_head": int(spec0.sum_out), "alg_bytes": db,
+               "GB/s": round(db / ((part_us + comb_us) * 1e-6) / 1e9, 1)}
+
     # ---- CPU baseline: the oracle on the host cores --------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -439,6 +479,8 @@ def main():
     }
     if hit is not None:
         out["hit_rate_kernel"] = hit
+    if dec is not None:
+        out["decode_over_compressed_cache"] = dec
     print(json.dumps(out), flush=True)
 
 

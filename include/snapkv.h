@@ -196,6 +196,36 @@ int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t 
                     void *stream);
 
 /*
+ * Decode attention over the compressed cache -- the step after the compression (page
+ * section デコード速度とメモリ効率; the KV-cache chapter's decode step): one new query row
+ * per (request, query head) attends to every cached row of its KV head,
+ *   out[r][h] = sum_j softmax_j(q[r][h] . K[g][j] / sqrt(d)) V[g][j],  g = h / G,
+ * over the rows j of request r: cu_rows_host[r] .. cu_rows_host[r+1]-1 (snapkv_plan's
+ * cu_out for a cache that snapkv_compress wrote; rows appended since are just a longer
+ * range).  A request with no rows gets zeros.
+ *   q      : [B][H_q][d] of the problem's dtype, contiguous.
+ *   K, V   : element (g, t, c) at g*kv_head_stride + t*kv_token_stride + c (K_out/V_out
+ *            of snapkv_compress: kv_head_stride = sum_out*d, kv_token_stride = d).
+ *   out    : float32 [B][H_q][d].
+ *   ws     : snapkv_decode_plan's ws_bytes (no zero-fill needed), 256-byte aligned.
+ * Supported: rows of 256 bytes (bf16 d = 128, fp32 d = 64); otherwise SNAPKV_EUNSUPPORTED.
+ */
+typedef struct {
+    int32_t batch;            /* B >= 1 */
+    int32_t num_q_heads;      /* H_q */
+    int32_t num_kv_heads;     /* H_kv, H_q % H_kv == 0 */
+    int32_t head_dim;         /* d */
+    int32_t dtype;            /* snapkv_dtype */
+    int64_t kv_head_stride;   /* elements */
+    int64_t kv_token_stride;  /* elements, >= d */
+    const int64_t *cu_rows_host; /* host [B+1], non-decreasing, cu_rows_host[0] >= 0 */
+} snapkv_decode_problem;
+
+int snapkv_decode_plan(const snapkv_decode_problem *dp, size_t *ws_bytes);
+int snapkv_decode(const snapkv_decode_problem *dp, const void *q, const void *K, const void *V, float *out, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
  * Kernel trace (profiling hook).  While a trace is open on the calling thread,
  * the i-th kernel a snapkv_* call launches (i < n_pairs) carries events[2i] and
  * events[2i+1] as the start and stop events of its dispatch
@@ -218,7 +248,9 @@ typedef enum {
     SNAPKV_K_GATHER = 7,      /* kv_gather */
     SNAPKV_K_SUM_CHUNKS = 8,  /* sum of the votes of the row chunks (G * L_obs > 32) */
     SNAPKV_K_SELECT_TILES = 9, /* topk_select of segments longer than 32768 positions (4 phases) */
-    SNAPKV_K_HIT_RATE = 10     /* snapkv_hit_rate */
+    SNAPKV_K_HIT_RATE = 10,    /* snapkv_hit_rate */
+    SNAPKV_K_DECODE = 11,      /* snapkv_decode: split-K partials */
+    SNAPKV_K_DECODE_COMBINE = 12 /* snapkv_decode: merge of the splits */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -24,7 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-           "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate",
+           "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate", "snapkv_decode_plan", "snapkv_decode",
            "snapkv_trace_begin", "snapkv_trace_end", "snapkv_kernel_name",
            "snapkv_strerror", "snapkv_last_error", "snapkv_version")
 
@@ -60,6 +60,12 @@ _lib = None
 _lock = threading.Lock()
 
 
+class DecodeProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("kv_head_stride", ctypes.c_int64),
+                ("kv_token_stride", ctypes.c_int64), ("cu_rows_host", ctypes.POINTER(ctypes.c_int64))]
+
+
 def load() -> ctypes.CDLL:
     """Load libsnapkv.so; raises if it has not been built."""
     global _lib
@@ -79,8 +85,12 @@ def load() -> ctypes.CDLL:
             lib.snapkv_scores_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_compress_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_hit_rate.argtypes = [P, vp, vp, ctypes.c_double, vp, vp]
+            DP = ctypes.POINTER(DecodeProblem)
+            lib.snapkv_decode_plan.argtypes = [DP, ctypes.POINTER(sz)]
+            lib.snapkv_decode.argtypes = [DP, vp, vp, vp, vp, vp, sz, vp]
             for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-                      "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate"):
+                      "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate", "snapkv_decode_plan",
+                      "snapkv_decode"):
                 getattr(lib, f).restype = ctypes.c_int
             lib.snapkv_strerror.argtypes = [ctypes.c_int]
             lib.snapkv_strerror.restype = ctypes.c_char_p
@@ -304,3 +314,32 @@ def hit_rate_counts(a_cur, idx, q_obs, K, cu_seqlens=None, *, obs_window=32, poo
                                 _stream())
     _check(st, "snapkv_hit_rate")
     return counts
+
+
+def decode(q, K, V, cu_rows, ws=None):
+    """snapkv_decode: attention of one query row per (request, query head), q [B, H_q, d],
+    over the cached rows cu_rows[r] .. cu_rows[r+1]-1 of K/V [H_kv, T, d] (any strides with
+    a contiguous last dim; K_out/V_out of compress with its cu_out).  Returns float32
+    [B, H_q, d]."""
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, H_q, d]")
+    if K.dim() != 3 or K.stride(2) != 1 or V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
+        raise ValueError("K, V must be [H_kv, T, d] with equal strides and a contiguous last dim")
+    if q.dtype != K.dtype:
+        raise ValueError("q and K must share a dtype")
+    cu = np.ascontiguousarray(np.asarray(cu_rows, dtype=np.int64))
+    dp = DecodeProblem()
+    dp.batch, dp.num_q_heads, dp.num_kv_heads, dp.head_dim = q.shape[0], q.shape[1], K.shape[0], K.shape[2]
+    dp.dtype = _dtype_code(K)
+    dp.kv_head_stride, dp.kv_token_stride = K.stride(0), K.stride(1)
+    dp.cu_rows_host = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    lib = load()
+    need = ctypes.c_size_t()
+    _check(lib.snapkv_decode_plan(ctypes.byref(dp), ctypes.byref(need)), "snapkv_decode_plan")
+    if ws is None:
+        ws = torch.empty(max(need.value, 256), dtype=torch.uint8, device=K.device)
+    out = torch.empty(q.shape, dtype=torch.float32, device=K.device)
+    st = lib.snapkv_decode(ctypes.byref(dp), _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(ws),
+                           ctypes.c_size_t(ws.numel()), _stream())
+    _check(st, "snapkv_decode")
+    return out

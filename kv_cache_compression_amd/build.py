@@ -12,7 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "obs_score.hip", "select_gather.hip"]
+SOURCES = ["api.hip", "obs_score.hip", "select_gather.hip", "decode.hip"]
 LIB = os.path.join(PKG, "libsnapkv.so")
 
 HIPCC_FLAGS = [

@@ -719,6 +719,129 @@ int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t 
     return finish(SNAPKV_OK);
 }
 
+// ---- decode attention ----
+
+// Cached rows per decode workgroup (split-K): at least 256, more when the longest request
+// would otherwise give over ~1024 workgroups, in multiples of the rows one pass covers.
+constexpr int kDecSplitMin = 256;
+
+struct DecodePlan {
+    int B, Hq, Hkv, G, d, dtype, head_tile, n_hchunks, max_splits, split_rows;
+    int64_t head_stride, token_stride;
+    std::vector<ReqTable> groups;
+    size_t ws_bytes;
+};
+
+static int make_decode_plan(const snapkv_decode_problem *dp, DecodePlan *pl) {
+    g_last_error.clear();
+    if (!dp) return fail(SNAPKV_EINVAL, "problem is NULL");
+    DecodePlan &p = *pl;
+    p.B = dp->batch;
+    p.Hq = dp->num_q_heads;
+    p.Hkv = dp->num_kv_heads;
+    p.d = dp->head_dim;
+    p.dtype = dp->dtype;
+    p.head_stride = dp->kv_head_stride;
+    p.token_stride = dp->kv_token_stride;
+    if (p.B < 1) return fail(SNAPKV_EINVAL, "batch must be >= 1");
+    if (p.Hq < 1 || p.Hkv < 1 || p.Hq % p.Hkv) return fail(SNAPKV_EINVAL, "num_q_heads must be a multiple of num_kv_heads");
+    if (p.dtype != SNAPKV_F32 && p.dtype != SNAPKV_BF16) return fail(SNAPKV_EINVAL, "dtype must be F32 or BF16");
+    if (p.d < 1) return fail(SNAPKV_EINVAL, "head_dim must be >= 1");
+    const int esz = p.dtype == SNAPKV_F32 ? 4 : 2;
+    if (p.d * esz != 256) return fail(SNAPKV_EUNSUPPORTED, "decode supports rows of 256 bytes (bf16 d=128, fp32 d=64)");
+    if (p.token_stride < p.d || p.head_stride < 0) return fail(SNAPKV_EINVAL, "kv strides must be >= head_dim and >= 0");
+    if ((p.token_stride * esz) % 16 || (p.head_stride * esz) % 16)
+        return fail(SNAPKV_EINVAL, "kv strides must keep rows 16-byte aligned");
+    if (!dp->cu_rows_host) return fail(SNAPKV_EINVAL, "cu_rows_host is NULL");
+    const int64_t *cu = dp->cu_rows_host;
+    if (cu[0] < 0) return fail(SNAPKV_EINVAL, "cu_rows_host[0] must be >= 0");
+    int64_t max_rows = 0;
+    for (int r = 0; r < p.B; ++r) {
+        const int64_t n = cu[r + 1] - cu[r];
+        if (n < 0) return fail(SNAPKV_EINVAL, "cu_rows_host must be non-decreasing");
+        if (n > 0x3fffffff) return fail(SNAPKV_EUNSUPPORTED, "too many rows in one request");
+        if (n > max_rows) max_rows = n;
+    }
+    p.G = p.Hq / p.Hkv;
+    p.head_tile = p.G >= 8 ? 8 : (p.G >= 4 ? (p.G == 4 ? 4 : 8) : (p.G == 1 ? 1 : (p.G == 2 ? 2 : 4)));
+    p.n_hchunks = (p.G + p.head_tile - 1) / p.head_tile;
+    const int items = (p.B < kMaxReq ? p.B : kMaxReq) * p.Hkv * p.n_hchunks;
+    const int rpi = decode_rows_per_iter();
+    int64_t split = (max_rows * items + 1023) / 1024;
+    split = (split + rpi - 1) / rpi * rpi;
+    if (split < kDecSplitMin) split = kDecSplitMin;
+    if ((max_rows + split - 1) / split > decode_max_splits())
+        split = (max_rows + decode_max_splits() - 1) / decode_max_splits();
+    p.split_rows = (int)((split + rpi - 1) / rpi * rpi);
+    p.max_splits = (int)((max_rows + p.split_rows - 1) / p.split_rows);
+    if (p.max_splits < 1) p.max_splits = 1;
+    p.groups.clear();
+    for (int r0 = 0; r0 < p.B; r0 += kMaxReq) {
+        ReqTable rt;
+        memset(&rt, 0, sizeof rt);
+        rt.n = p.B - r0 < kMaxReq ? p.B - r0 : kMaxReq;
+        for (int i = 0; i < rt.n; ++i) {
+            rt.L[i] = (int32_t)(cu[r0 + i + 1] - cu[r0 + i]);
+            rt.tok0[i] = cu[r0 + i];
+            rt.qi[i] = r0 + i;
+        }
+        p.groups.push_back(rt);
+    }
+    p.ws_bytes = align_up(sizeof(float) * (size_t)items * p.max_splits * p.head_tile * (p.d + 2));
+    return SNAPKV_OK;
+}
+
+int snapkv_decode_plan(const snapkv_decode_problem *dp, size_t *ws_bytes) {
+    DecodePlan p;
+    const int st = make_decode_plan(dp, &p);
+    if (!st && ws_bytes) *ws_bytes = p.ws_bytes;
+    return st;
+}
+
+int snapkv_decode(const snapkv_decode_problem *dp, const void *q, const void *K, const void *V, float *out, void *ws,
+                  size_t ws_bytes, void *stream) {
+    DecodePlan p;
+    int st = make_decode_plan(dp, &p);
+    if (!st) st = check_ptr(q, "q");
+    if (!st) st = check_ptr(K, "K");
+    if (!st) st = check_ptr(V, "V");
+    if (!st) st = check_ptr(out, "out");
+    if (!st && (!ws || (uintptr_t)ws % kWsAlign)) st = fail(SNAPKV_EWORKSPACE, "workspace missing or not 256-byte aligned");
+    if (!st && ws_bytes < p.ws_bytes) st = fail(SNAPKV_EWORKSPACE, "workspace too small: need " + std::to_string(p.ws_bytes) + " bytes");
+    if (st) return st;
+    DevInfo di;
+    st = device_info(&di);
+    if (st) return st;
+    for (const ReqTable &rt : p.groups) {
+        DecodeParams dpar;
+        memset(&dpar, 0, sizeof dpar);
+        dpar.q = q;
+        dpar.K = K;
+        dpar.V = V;
+        dpar.part = (float *)ws;
+        dpar.out = out;
+        dpar.head_stride = p.head_stride;
+        dpar.token_stride = p.token_stride;
+        dpar.Hq = p.Hq;
+        dpar.Hkv = p.Hkv;
+        dpar.G = p.G;
+        dpar.d = p.d;
+        dpar.n_hchunks = p.n_hchunks;
+        dpar.head_tile = p.head_tile;
+        dpar.max_splits = p.max_splits;
+        dpar.split_rows = p.split_rows;
+        dpar.c = (float)(1.4426950408889634 / sqrt((double)p.d));
+        dpar.rt = rt;
+        st = launch(SNAPKV_K_DECODE, decode_partial_kernel_for(p.dtype, p.head_tile),
+                    dim3(p.max_splits, rt.n * p.Hkv * p.n_hchunks), dim3(decode_threads()), &dpar, (hipStream_t)stream);
+        if (!st)
+            st = launch(SNAPKV_K_DECODE_COMBINE, decode_combine_kernel_ptr(), dim3(rt.n * p.Hq), dim3(128), &dpar,
+                        (hipStream_t)stream);
+        if (st) return finish(st);
+    }
+    return finish(SNAPKV_OK);
+}
+
 int snapkv_trace_begin(void *const *events, int n_pairs) {
     g_last_error.clear();
     if (!events || n_pairs < 1) return fail(SNAPKV_EINVAL, "trace needs events and n_pairs >= 1");
@@ -751,6 +874,8 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_SUM_CHUNKS: return "sum_chunks";
         case SNAPKV_K_SELECT_TILES: return "topk_select_tiles";
         case SNAPKV_K_HIT_RATE: return "hit_rate";
+        case SNAPKV_K_DECODE: return "decode_attention";
+        case SNAPKV_K_DECODE_COMBINE: return "decode_combine";
         default: return "unknown";
     }
 }

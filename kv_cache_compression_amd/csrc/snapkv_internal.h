@@ -159,6 +159,22 @@ struct HitParams {
 };
 const void *hit_kernel();
 
+struct DecodeParams {
+    const void *q;              // [B][H_q][d]
+    const void *K, *V;          // cache rows (token-packed, as for compression)
+    float *part;                // [items][max_splits][head_tile][d + 2] partials
+    float *out;                 // [B][H_q][d] fp32
+    int64_t head_stride, token_stride;  // elements
+    int32_t Hq, Hkv, G, d, n_hchunks, head_tile, max_splits, split_rows;
+    float c;                    // log2(e) / sqrt(d)
+    ReqTable rt;                // L = cached rows, tok0 = first row, qi = request
+};
+const void *decode_partial_kernel_for(int dtype, int head_tile);
+const void *decode_combine_kernel_ptr();
+int decode_threads();
+int decode_rows_per_iter();
+int decode_max_splits();      // splits one combine workgroup merges
+
 struct GatherParams {
     const void *K, *V;
     const int32_t *idx;

@@ -268,6 +268,59 @@ def test_hit_rate_beyond_one_bitmap_span():
     assert hits / above == oracle.hit_rate(a[0], mask, 0.05)
 
 
+# ---- decode attention over the compressed cache ------------------------------------------------
+
+DECODE_CASES = [
+    # name, lengths, Hq, Hkv, d, dtype, w, ratio
+    ("dec_mha_bf16", [3000, 1400], 4, 4, 128, "bf16", 32, 0.2),
+    ("dec_gqa4_bf16", [9000], 8, 2, 128, "bf16", 32, 0.3),     # several splits per head
+    ("dec_gqa3_bf16", [2000, 700], 6, 2, 128, "bf16", 16, 0.5),  # 3 heads per KV head (tile of 4)
+    ("dec_gqa16_bf16", [1500], 16, 1, 128, "bf16", 8, 0.5),    # two head tiles of 8
+    ("dec_f32_d64", [1800, 64], 4, 2, 64, "f32", 32, 0.4),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_over_compressed_cache(case):
+    """snapkv_decode over snapkv_compress's K_out/V_out equals the oracle's decode attention
+    over the same rows (fp32 accumulation: |gpu - ref| <= 1e-4 |ref| + 1e-5)."""
+    name, lengths, Hq, Hkv, d, dt, w, ratio = case
+    snap = _snap()
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=7, ratio=ratio, n_plant=4, name=name)
+    _say("case %s" % name)
+    x = synth.make_inputs(wl)
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    res = snap.compress(q, K, V, x["cu_seqlens"], obs_window=w, pool_kernel=7, ratio=ratio)
+    rng = np.random.default_rng(30)
+    qd = rng.standard_normal((len(lengths), Hq, d)).astype(np.float32) * 2
+    qd = synth.round_bf16(qd) if dt == "bf16" else qd
+    out = snap.decode(to_torch(qd), res["K_out"], res["V_out"], res["cu_out"])
+    torch.cuda.synchronize()
+    ref = oracle.decode_all(qd, to_numpy_bits(res["K_out"]), to_numpy_bits(res["V_out"]), res["cu_out"])
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-4, atol=1e-5)
+
+
+def test_decode_empty_request_and_token_major_cache():
+    """A request with no cached rows gets zeros; a token-major cache view gives the same result."""
+    snap = _snap()
+    rng = np.random.default_rng(31)
+    Hq, Hkv, d, T = 4, 2, 128, 700
+    cu = np.array([0, 300, 300, 700], np.int64)
+    Kn = synth.round_bf16(rng.standard_normal((Hkv, T, d)).astype(np.float32))
+    Vn = synth.round_bf16(rng.standard_normal((Hkv, T, d)).astype(np.float32))
+    qn = synth.round_bf16(rng.standard_normal((3, Hq, d)).astype(np.float32))
+    K, V, q = to_torch(Kn), to_torch(Vn), to_torch(qn)
+    out = snap.decode(q, K, V, cu).cpu().numpy()
+    Kt = K.transpose(0, 1).contiguous().transpose(0, 1)
+    Vt = V.transpose(0, 1).contiguous().transpose(0, 1)
+    out_t = snap.decode(q, Kt, Vt, cu).cpu().numpy()
+    torch.cuda.synchronize()
+    ref = oracle.decode_all(qn, Kn, Vn, cu)
+    assert not out[1].any()
+    np.testing.assert_allclose(out, ref, rtol=1e-4, atol=1e-5)
+    np.testing.assert_array_equal(out, out_t)
+
+
 def test_prefix_only_variant():
     wl = synth.custom([3000, 1500], 8, 2, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8,
                       name="prefix_only")
