@@ -10,8 +10,8 @@ __version__ = "0.1.0"
 
 def __getattr__(name):
     # The binding (and torch) load on first use, so `synth` stays importable alone.
-    if name in ("compress", "scores", "select", "gather", "make_spec", "workspace", "load", "SnapKVError",
-                "Spec", "Problem"):
+    if name in ("compress", "scores", "select", "gather", "decode", "hit_rate_counts", "make_spec", "workspace",
+                "load", "SnapKVError", "Spec", "Problem", "DecodeProblem"):
         from . import _lib
         return getattr(_lib, name)
     raise AttributeError(name)

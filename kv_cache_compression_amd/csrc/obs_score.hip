@@ -159,6 +159,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     constexpr int NCH = ROWB / 16;      // 16-byte chunks per row
     constexpr bool QLDS = WR == 1 && !STAGED;  // window queries read from LDS (else VGPRs)
     static_assert(ROWB % 64 == 0, "row must be a multiple of 64 bytes");
+    static_assert(WR == 1, "one row wave: each wave holds every row of the chunk");
     static_assert(!STAGED || (ROWB == 256 && NQ == 4), "staged tiles are 16 rows of 256 bytes");
     // LDS rows padded by one chunk so the 16 rows of an MFMA operand hit distinct banks
     __shared__ u32x4_t sh_q[QLDS ? MROWS : 1][NCH + 1];
@@ -168,7 +169,6 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     __shared__ float sh_l[WK][MROWS];
     __shared__ float sh_rowm[MROWS];
     __shared__ float sh_f[MROWS];
-    __shared__ float sh_v[WR > 1 ? WR : 1][WR > 1 ? SLAB : 1];
     __shared__ int sh_wrow[kMaxRows];  // window row (row % L_obs) of each query row, for the causal mask
 
     const int tid = threadIdx.x;
@@ -502,26 +502,10 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                     static_for<4>([&](auto i) { v = fmaf(S[rt][ct][i()], f[rt][i], v); });
                 });
                 v = cross_row_sum4(v);
-                if constexpr (WR == 1) {
-                    // this wave holds every row: its 16 lanes of group 0 store the tile's votes
-                    const int j = tile_key(ct) + n16;
-                    if (grp == 0 && j < P) vout[j] = v;
-                } else {
-                    if (grp == 0) sh_v[wr][(ct * WK + wk) * 16 + n16] = v;
-                }
+                // this wave holds every row: its 16 lanes of group 0 store the tile's votes
+                const int j = tile_key(ct) + n16;
+                if (grp == 0 && j < P) vout[j] = v;
             });
-            if constexpr (WR > 1) {
-                __syncthreads();
-                for (int t = tid; t < SLAB; t += NT) {
-                    const int j = key0 + t;
-                    if (j < P) {
-                        float a = sh_v[0][t];
-#pragma unroll
-                        for (int w2 = 1; w2 < WR; ++w2) a += sh_v[w2][t];
-                        vout[j] = a;
-                    }
-                }
-            }
             __syncthreads();
         }
     }

@@ -107,12 +107,6 @@ __device__ __forceinline__ void find_bin(const uint32_t *hist, uint32_t need, ui
     }
 }
 
-// Digit layout of the three passes.
-template <int PASS> struct Digit {
-    static constexpr int shift = PASS == 0 ? 20 : (PASS == 1 ? 9 : 0);
-    static constexpr uint32_t mask = PASS == 2 ? 0x1FFu : 0x7FFu;
-};
-
 // State of a selection: values v with (v & mask) > prefix are kept; of those equal to prefix,
 // the first `need` in position order are kept.
 struct Pivot {
