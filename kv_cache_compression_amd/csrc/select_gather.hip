@@ -233,18 +233,54 @@ __device__ __forceinline__ void select_resident(const SelectParams &p, uint32_t 
                                                 int k, int64_t base, int32_t *out) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     {
-        // votes -> LDS, R coalesced loads in flight per thread; histograms cleared meanwhile
+        // votes -> LDS, coalesced (16-byte loads when the segment is 16-byte aligned), all of a
+        // thread's loads in flight; histograms cleared meanwhile.  The AND / OR of the staged
+        // values is taken on the way: every pooled value is one of them, so bits they all share
+        // are shared by the pooled values too.
         const uint32_t *src = (const uint32_t *)((p.votes ? p.votes : p.pooled) + base);
-        uint32_t t[R];
-        static_for<R>([&](auto i) {
-            const int j = i() * kSelThreads + tid;
-            t[i()] = j < P ? src[j] : 0u;
-        });
-        for (int i = tid; i < 2 * kBins; i += kSelThreads) (&s.hist[0][0])[i] = 0;
-        static_for<R>([&](auto i) {
-            const int j = i() * kSelThreads + tid;
-            if (j < P) sdata[j] = t[i()];
-        });
+        uint32_t va = ~0u, vo = 0u;
+        if (((uintptr_t)src & 15) == 0) {
+            u32x4_t t[R / 4];
+            static_for<R / 4>([&](auto i) {
+                const int j = 4 * (i() * kSelThreads + tid);
+                if (j + 3 < P) {
+                    t[i()] = *(const u32x4_t *)(src + j);
+                } else {
+                    static_for<4>([&](auto e) { t[i()][e()] = j + e() < P ? src[j + e()] : 0u; });
+                }
+            });
+            for (int i = tid; i < 2 * kBins; i += kSelThreads) (&s.hist[0][0])[i] = 0;
+            static_for<R / 4>([&](auto i) {
+                const int j = 4 * (i() * kSelThreads + tid);
+                if (j + 3 < P) {
+                    *(u32x4_t *)(sdata + j) = t[i()];
+                } else {
+                    static_for<4>([&](auto e) {
+                        if (j + e() < P) sdata[j + e()] = t[i()][e()];
+                    });
+                }
+                static_for<4>([&](auto e) {
+                    if (j + e() < P) { va &= t[i()][e()] & 0x7FFFFFFFu; vo |= t[i()][e()] & 0x7FFFFFFFu; }
+                });
+            });
+        } else {
+            uint32_t t[R];
+            static_for<R>([&](auto i) {
+                const int j = i() * kSelThreads + tid;
+                t[i()] = j < P ? src[j] : 0u;
+            });
+            for (int i = tid; i < 2 * kBins; i += kSelThreads) (&s.hist[0][0])[i] = 0;
+            static_for<R>([&](auto i) {
+                const int j = i() * kSelThreads + tid;
+                if (j < P) {
+                    sdata[j] = t[i()];
+                    va &= t[i()] & 0x7FFFFFFFu;
+                    vo |= t[i()] & 0x7FFFFFFFu;
+                }
+            });
+        }
+        wave_and_or(va, vo);
+        if (lane == 0) { s.wand[wave] = va; s.wor[wave] = vo; }
     }
     __syncthreads();
     const int j0 = tid * R;
@@ -273,13 +309,6 @@ __device__ __forceinline__ void select_resident(const SelectParams &p, uint32_t 
     // Bits shared by every value need no radix pass: the first digit starts at the highest
     // bit where the values differ, which spreads the first histogram over many bins.
     uint32_t va = ~0u, vo = 0u;
-    static_for<R>([&](auto i) {
-        if (i() < nvalid) { va &= u[i()]; vo |= u[i()]; }
-    });
-    wave_and_or(va, vo);
-    if (lane == 0) { s.wand[wave] = va; s.wor[wave] = vo; }
-    __syncthreads();
-    va = ~0u; vo = 0u;
     static_for<kSelWaves>([&](auto w2) { va &= s.wand[w2()]; vo |= s.wor[w2()]; });
     const uint32_t diff = va ^ vo;  // bits on which the values differ
     Pivot pv;
