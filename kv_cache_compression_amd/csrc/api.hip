@@ -57,6 +57,62 @@ struct Plan {
     size_t off_long_state, off_ghist, off_cand, off_tilecnt, ws_bytes;
 };
 
+// Groups of at most kMaxReq requests, for the slab size of p.cfg.
+static int build_groups(Plan &p, const int32_t *cu) {
+    const int slab = p.cfg.slab_keys();
+    p.groups.clear();
+    p.max_group_slabs = 0;
+    p.max_group_segs = 0;
+    for (int r0 = 0; r0 < p.B; r0 += kMaxReq) {
+        Group gr;
+        memset(&gr, 0, sizeof gr);
+        const int n = p.B - r0 < kMaxReq ? p.B - r0 : kMaxReq;
+        gr.rt.n = n;
+        int64_t slabs = 0;
+        for (int i = 0; i < n; ++i) {
+            const int r = r0 + i;
+            gr.rt.L[i] = (int32_t)p.L[r];
+            gr.rt.k[i] = (int32_t)p.k[r];
+            gr.rt.qi[i] = r;
+            gr.rt.slab0[i] = (int32_t)slabs;
+            gr.rt.tok0[i] = cu[r];
+            gr.rt.pfx0[i] = p.cu_pfx[r];
+            gr.rt.k0[i] = p.cu_k[r];
+            gr.rt.out0[i] = p.cu_out[r];
+            const int64_t ns = (p.L[r] + slab - 1) / slab;
+            slabs += ns * p.Hkv;
+            if (ns > gr.max_ns) gr.max_ns = (int)ns;
+            if (p.P[r] > gr.max_P) gr.max_P = (int)p.P[r];
+        }
+        if (slabs * p.n_chunks > (1 << 30)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
+        gr.rt.slab0[n] = (int32_t)slabs;
+        gr.n_slabs = (int)slabs;
+        gr.out_rows = p.cu_out[r0 + n] - p.cu_out[r0];
+        p.groups.push_back(gr);
+        if (gr.n_slabs > p.max_group_slabs) p.max_group_slabs = gr.n_slabs;
+        if (n * p.Hkv > p.max_group_segs) p.max_group_segs = n * p.Hkv;
+    }
+    return SNAPKV_OK;
+}
+
+static int64_t pack_segments(const Plan &p, const Group &gr, int grid, int32_t *vb);
+
+// Estimated time of the fused scoring launches, in units of one key tile per wave: every grid
+// iteration streams its slabs (CTW tiles per wave) and then pays a fixed tail (row stats,
+// segment barrier, votes) of about ten tiles.  The grid is the 256 workgroups an MI355X keeps
+// resident (one per CU).
+static double fused_cost(const Plan &p) {
+    constexpr int kGrid = 256;
+    double cost = 0;
+    for (const Group &gr : p.groups) {
+        int32_t vb[kMaxReq + 1];
+        const int64_t slots = (int64_t)gr.max_ns * p.n_chunks > kGrid ? -1 : pack_segments(p, gr, kGrid, vb);
+        if (slots < 0) return 1e300;
+        cost += (double)((slots + kGrid - 1) / kGrid) * (p.cfg.ctw + 10);
+    }
+    return cost;
+}
+
 int make_plan(const snapkv_problem *pb, Plan *pl) {
     g_last_error.clear();
     if (!pb) return fail(SNAPKV_EINVAL, "problem is NULL");
@@ -140,39 +196,22 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     p.sum_k = p.cu_k[p.B];
     p.sum_out = p.cu_out[p.B];
 
-    // groups of at most kMaxReq requests
-    const int slab = p.cfg.slab_keys();
-    p.groups.clear();
-    p.max_group_slabs = 0;
-    p.max_group_segs = 0;
-    for (int r0 = 0; r0 < p.B; r0 += kMaxReq) {
-        Group gr;
-        memset(&gr, 0, sizeof gr);
-        const int n = p.B - r0 < kMaxReq ? p.B - r0 : kMaxReq;
-        gr.rt.n = n;
-        int64_t slabs = 0;
-        for (int i = 0; i < n; ++i) {
-            const int r = r0 + i;
-            gr.rt.L[i] = (int32_t)p.L[r];
-            gr.rt.k[i] = (int32_t)p.k[r];
-            gr.rt.qi[i] = r;
-            gr.rt.slab0[i] = (int32_t)slabs;
-            gr.rt.tok0[i] = cu[r];
-            gr.rt.pfx0[i] = p.cu_pfx[r];
-            gr.rt.k0[i] = p.cu_k[r];
-            gr.rt.out0[i] = p.cu_out[r];
-            const int64_t ns = (p.L[r] + slab - 1) / slab;
-            slabs += ns * p.Hkv;
-            if (ns > gr.max_ns) gr.max_ns = (int)ns;
-            if (p.P[r] > gr.max_P) gr.max_P = (int)p.P[r];
+    // groups of at most kMaxReq requests; rows of 256 bytes take the shorter slab when its
+    // slab counts pack into fewer grid iterations' worth of time (see fused_cost)
+    int st = build_groups(p, cu);
+    if (st) return st;
+    ObsConfig alt;
+    if (!(p.flags & SNAPKV_FLAG_TWO_PASS) && obs_config_short(p.dtype, p.d, &alt)) {
+        const double c0 = fused_cost(p);
+        const ObsConfig keep_cfg = p.cfg;
+        p.cfg = alt;
+        st = build_groups(p, cu);
+        if (st) return st;
+        if (!(fused_cost(p) < c0)) {
+            p.cfg = keep_cfg;
+            st = build_groups(p, cu);
+            if (st) return st;
         }
-        if (slabs * p.n_chunks > (1 << 30)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
-        gr.rt.slab0[n] = (int32_t)slabs;
-        gr.n_slabs = (int)slabs;
-        gr.out_rows = p.cu_out[r0 + n] - p.cu_out[r0];
-        p.groups.push_back(gr);
-        if (gr.n_slabs > p.max_group_slabs) p.max_group_slabs = gr.n_slabs;
-        if (n * p.Hkv > p.max_group_segs) p.max_group_segs = n * p.Hkv;
     }
     for (int r = 0; r < p.B; ++r)
         if (cu[r + 1] > 0x7fffffff - 1) return fail(SNAPKV_EUNSUPPORTED, "token count exceeds int32");
@@ -300,23 +339,24 @@ int launch(int id, const void *kernel, dim3 grid, dim3 block, void *arg, hipStre
 
 int run_pool(const Plan &p, const Group &gr, const float *votes, float *pooled, hipStream_t stream);
 
-// Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
-// Whether a fused launch over the group runs without waits that span grid iterations:
-// work item v (a (slab, row chunk) pair) runs in iteration v / grid, and each segment's
-// items must lie in one iteration.  (A segment spanning two iterations still completes,
-// since no segment has more items than the grid, but its barrier then waits for the next
-// iteration's workgroups, which serialises the iterations.)
-static bool fused_fits(const Plan &p, const Group &gr, int grid) {
-    const int C = p.n_chunks;
+// Slot layout of a fused launch that needs several grid iterations: each (request, KV head)
+// segment of z items starts at the next iteration boundary when it would cross one, so all
+// of its items run in the same iteration (its barrier never waits for a later iteration).
+// The device side (packed_item) inverts this layout.  Returns the number of slots.
+static int64_t pack_segments(const Plan &p, const Group &gr, int grid, int32_t *vb) {
+    const int slab = p.cfg.slab_keys();
+    int64_t pos = 0;
     for (int i = 0; i < gr.rt.n; ++i) {
-        const int ns = (gr.rt.L[i] + p.cfg.slab_keys() - 1) / p.cfg.slab_keys();
+        vb[i] = (int32_t)pos;
+        const int64_t z = (int64_t)((gr.rt.L[i] + slab - 1) / slab) * p.n_chunks;
+        if (z == 0) continue;
         for (int g = 0; g < p.Hkv; ++g) {
-            const int64_t v0 = ((int64_t)gr.rt.slab0[i] + (int64_t)g * ns) * C;
-            const int64_t v1 = v0 + (int64_t)ns * C;  // exclusive
-            if (ns > 0 && v0 / grid != (v1 - 1) / grid) return false;
+            if (pos % grid + z > grid) pos += grid - pos % grid;
+            pos += z;
         }
     }
-    return true;
+    vb[gr.rt.n] = (int32_t)pos;
+    return pos;
 }
 
 // Votes of every group (into `votes`); with `pool`, also the pooled votes (into `pooled`).
@@ -334,7 +374,7 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
     float2 *partial = (float2 *)(ws + p.off_partial);
     float2 *merged = (float2 *)(ws + p.off_merged);
     float *planes = C > 1 ? (float *)(ws + p.off_planes) : votes;
-    const void *kf = obs_kernel(p.dtype, p.d, kFused, keep);
+    const void *kf = obs_kernel(p.dtype, p.d, cfg, kFused, keep);
     const int occ = occupancy(kf, cfg.threads());
     const int resident = occ * di.cus;
     for (const Group &gr : p.groups) {
@@ -367,22 +407,35 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
         op.lse_scale = (float)sqrt((double)p.d);
         op.rt = gr.rt;
         const int64_t items = (int64_t)gr.n_slabs * C;
-        const int grid = items < resident ? (int)items : resident;
         // The fused kernel's grid never exceeds what the device keeps resident, and no
-        // segment has more work items than that grid, so every segment barrier completes.
-        const bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && (int64_t)gr.max_ns * C <= resident &&
-                           fused_fits(p, gr, grid);
+        // segment has more work items than that grid; with more items than the grid, the
+        // packed layout keeps each segment inside one iteration, so every segment barrier
+        // completes within its iteration.
+        // A packing that leaves more than a fifth of the slots idle loses to the two-pass path
+        // (which reads K twice but keeps every workgroup busy).
+        bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && (int64_t)gr.max_ns * C <= resident;
+        const int grid = items < resident ? (int)items : resident;
+        if (fused && items > resident) {
+            op.pack_grid = resident;
+            const int64_t slots = pack_segments(p, gr, resident, op.vb);
+            if (slots > 0x7fffffff) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
+            const int64_t iters = (slots + resident - 1) / resident;
+            if (iters * resident * 4 > items * 5) {
+                fused = false;
+                op.pack_grid = 0;
+            }
+        }
         const int n_seg = gr.rt.n * p.Hkv;
         if (lse) {
             // the caller's row stats: one read of K, no barrier
-            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, kVotes, keep), dim3((unsigned)items),
+            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, cfg, kVotes, keep), dim3((unsigned)items),
                         dim3(cfg.threads()), &op, stream);
             if (st) return st;
         } else if (fused) {
             st = launch(SNAPKV_K_OBS_FUSED, kf, dim3(grid), dim3(cfg.threads()), &op, stream);
             if (st) return st;
         } else {
-            st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, kStats, keep), dim3((unsigned)items),
+            st = launch(SNAPKV_K_OBS_STATS, obs_kernel(p.dtype, p.d, cfg, kStats, keep), dim3((unsigned)items),
                         dim3(cfg.threads()), &op, stream);
             if (st) return st;
             MergeParams mp;
@@ -399,7 +452,7 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
             st = launch(SNAPKV_K_STATS_MERGE, merge_kernel(), dim3(n_seg * C, (p.M_pad + 3) / 4), dim3(256), &mp,
                         stream);
             if (st) return st;
-            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, kVotes, keep), dim3((unsigned)items),
+            st = launch(SNAPKV_K_OBS_VOTES, obs_kernel(p.dtype, p.d, cfg, kVotes, keep), dim3((unsigned)items),
                         dim3(cfg.threads()), &op, stream);
             if (st) return st;
         }

@@ -121,6 +121,37 @@ __device__ inline SlabPos decode_slab(const ReqTable &rt, int s, int slab_keys) 
     return p;
 }
 
+// Item order of a packed fused launch.  Request i's segments (one per KV head, z = slabs x
+// row chunks items each) follow each other from slot vb[i]; a segment that would cross an
+// iteration boundary starts at the next boundary instead, so the slots it skips stay idle.
+// Every segment then runs within one iteration of the grid, all of its workgroups at once.
+// Returns the item (slab * chunks + chunk) of slot u, or -1 for an idle slot.
+__device__ inline int packed_item(const ObsParams &p, int u, int C, int slab_keys) {
+    const int grid = p.pack_grid;
+    if (grid == 0) return u;
+    int r = 0;
+    while (r + 1 < p.rt.n && p.vb[r + 1] <= u) ++r;
+    const int ns = (p.rt.L[r] + slab_keys - 1) / slab_keys, z = ns * C;
+    const int base = p.vb[r], o0 = base % grid;
+    const int fit0 = (grid - o0) / z;  // segments that fit in the first iteration
+    const int h0 = fit0 < p.Hkv ? fit0 : p.Hkv;
+    int g, within;
+    if (u - base < h0 * z) {
+        g = (u - base) / z;
+        within = u - base - g * z;
+    } else {
+        const int next = base - o0 + grid;  // first slot of the next iteration
+        if (u < next) return -1;
+        const int it = (u - next) / grid, o = (u - next) - it * grid;
+        const int gi = o / z;
+        if (gi >= grid / z) return -1;
+        g = h0 + it * (grid / z) + gi;
+        if (g >= p.Hkv) return -1;
+        within = o - gi * z;
+    }
+    return (p.rt.slab0[r] + g * ns) * C + within;
+}
+
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
 // Key loads: non-temporal when every key is read once, cached when the row chunks of a
@@ -185,7 +216,10 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     const int C = p.n_chunks;
     const int nb = gridDim.x;
     const int b0 = (C == 1 || (nb & 7)) ? (int)blockIdx.x : ((int)blockIdx.x & 7) * (nb >> 3) + ((int)blockIdx.x >> 3);
-    for (int v = b0; v < p.n_slabs * C; v += nb) {
+    const int n_slots = p.pack_grid ? p.vb[p.rt.n] : p.n_slabs * C;
+    for (int u = b0; u < n_slots; u += nb) {
+        const int v = packed_item(p, u, C, SLAB);
+        if (v < 0) continue;
         const int s = v / C, chunk = v - (v / C) * C;
         const SlabPos sp = decode_slab(p.rt, s, SLAB);
         const int cbase = chunk * MROWS;                          // first query row of the chunk
@@ -436,14 +470,26 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             // Merge the segment's row stats; factor for this slab's resident weights.
             constexpr int TPR = NT / MROWS;  // threads per row (power of two)
             const int row = tid / TPR, sub = tid - (tid / TPR) * TPR;
+            // A thread's slabs are read kMergeBatch at a time, all loads in flight together (an
+            // index past the segment re-reads its last slab and is then ignored): long segments
+            // cost a few round trips, not one per slab.
+            constexpr int kMergeBatch = 8;
             float mm = neg_inf(), ll = 0.f;
             if (row < Mc) {
-                for (int s2 = sub; s2 < sp.ns; s2 += TPR) {
-                    const uint64_t bits = __hip_atomic_load(
-                        (uint64_t *)&p.partial[((int64_t)(sp.seg_slab0 + s2) * C + chunk) * p.M_pad + row],
-                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    const float2 pr = __builtin_bit_cast(float2, bits);
-                    merge_stats(mm, ll, pr.x, pr.y, c);
+                for (int s0 = sub; s0 < sp.ns; s0 += kMergeBatch * TPR) {
+                    uint64_t bits[kMergeBatch];
+                    static_for<kMergeBatch>([&](auto b) {
+                        const int s2 = s0 + b() * TPR < sp.ns ? s0 + b() * TPR : sp.ns - 1;
+                        bits[b()] = __hip_atomic_load(
+                            (uint64_t *)&p.partial[((int64_t)(sp.seg_slab0 + s2) * C + chunk) * p.M_pad + row],
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    });
+                    static_for<kMergeBatch>([&](auto b) {
+                        if (s0 + b() * TPR < sp.ns) {
+                            const float2 pr = __builtin_bit_cast(float2, bits[b()]);
+                            merge_stats(mm, ll, pr.x, pr.y, c);
+                        }
+                    });
                 }
             }
 #pragma unroll
@@ -570,21 +616,30 @@ static const void *pick_mode(int mode) {
     }
 }
 
+// Rows of 256 bytes also come with 12 key tiles per wave (1536-key slabs), for segments
+// whose 2048-key slab count packs badly into the grid's iterations.
+bool obs_config_short(int dtype, int d, ObsConfig *cfg) {
+    if (!obs_config(dtype, d, cfg) || d * (dtype == 0 ? 4 : 2) != 256) return false;
+    cfg->ctw = 12;
+    return true;
+}
+
 template <typename T, int D, bool KEEP>
-static const void *pick_keep(int mode) {
-    if constexpr (D * sizeof(T) == 256) return pick_mode<T, D, 16, true, KEEP>(mode);
+static const void *pick_keep(int mode, int ctw) {
+    if constexpr (D * sizeof(T) == 256)
+        return ctw == 12 ? pick_mode<T, D, 12, true, KEEP>(mode) : pick_mode<T, D, 16, true, KEEP>(mode);
     else if constexpr (D * sizeof(T) < 256) return pick_mode<T, D, 16, false, KEEP>(mode);
     else return pick_mode<T, D, 8, false, KEEP>(mode);
 }
 
 template <typename T, int D>
-static const void *pick(int mode, bool keep) {
-    return keep ? pick_keep<T, D, true>(mode) : pick_keep<T, D, false>(mode);
+static const void *pick(int mode, bool keep, int ctw) {
+    return keep ? pick_keep<T, D, true>(mode, ctw) : pick_keep<T, D, false>(mode, ctw);
 }
 
-const void *obs_kernel(int dtype, int d, int mode, bool keep) {
-    if (dtype == 1) return d == 64 ? pick<__bf16, 64>(mode, keep) : pick<__bf16, 128>(mode, keep);
-    return d == 64 ? pick<float, 64>(mode, keep) : pick<float, 128>(mode, keep);
+const void *obs_kernel(int dtype, int d, const ObsConfig &cfg, int mode, bool keep) {
+    if (dtype == 1) return d == 64 ? pick<__bf16, 64>(mode, keep, cfg.ctw) : pick<__bf16, 128>(mode, keep, cfg.ctw);
+    return d == 64 ? pick<float, 64>(mode, keep, cfg.ctw) : pick<float, 128>(mode, keep, cfg.ctw);
 }
 
 }  // namespace snapkv

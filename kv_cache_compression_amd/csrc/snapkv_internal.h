@@ -64,6 +64,12 @@ struct ObsParams {
     int64_t vplane;             // floats between the votes planes of consecutive chunks
     const float *lse;           // kVotes: caller's row log-sum-exp [B][H_q][L_obs] instead of merged
     float lse_scale;            // sqrt(d): lse * lse_scale * c = lse * log2(e)
+    // Packed item order (kFused over several grid iterations): request i's items start at
+    // slot vb[i] of a sequence of pack_grid-slot iterations, and no (request, KV head)
+    // segment crosses an iteration boundary (see packed_item).  pack_grid = 0: items in
+    // their natural order, slot = item.
+    int32_t pack_grid;
+    int32_t vb[kMaxReq + 1];
     ReqTable rt;
 };
 
@@ -81,8 +87,10 @@ struct ObsConfig {
 
 // Chooses the tile shape for (dtype, d); false if unsupported.
 bool obs_config(int dtype, int d, ObsConfig *cfg);
+// The shorter-slab shape for (dtype, d), where one exists (rows of 256 bytes).
+bool obs_config_short(int dtype, int d, ObsConfig *cfg);
 // Kernel entry of the chosen instantiation; keep = cached key loads.
-const void *obs_kernel(int dtype, int d, int mode, bool keep);
+const void *obs_kernel(int dtype, int d, const ObsConfig &cfg, int mode, bool keep);
 
 struct MergeParams {
     const float2 *partial;

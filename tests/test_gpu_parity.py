@@ -6,6 +6,7 @@ ratio and budget modes, ragged batches and the degenerate cases.  The five
 standard workloads run at full size in the launch configuration the benchmark
 times, checked on sampled (request, KV head) pairs the oracle computes one by one.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -113,6 +114,54 @@ def test_small_shapes(case):
                       n_plant=n_plant, name=name)
     x, _ = run_and_check(wl)
     run_and_check(wl, two_pass=True, inputs=x)
+
+
+# Fused scoring over several grid iterations of 256 workgroups: segments (KV heads) of
+# 24, 48 and 16 items (3 requests, 8 row chunks), and of 160 items (one per iteration),
+# are laid out so that none crosses an iteration boundary.
+PACKED = [
+    # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant
+    ("packed_varlen_chunks8", [5000, 11000, 3000], 32, 4, 128, "bf16", 32, 7, 0.05, None, 8),
+    ("packed_one_segment_per_iteration", [40000], 64, 2, 128, "bf16", 8, 7, 0.05, None, 8),
+]
+
+
+def _launched_kernels(fn):
+    """Kernel ids that fn's library calls launched (through the library's kernel trace)."""
+    lib = _snap().load()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    n = 64
+    ev = (ctypes.c_void_p * (2 * n))()
+    for i in range(2 * n):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        ev[i] = h
+    try:
+        assert lib.snapkv_trace_begin(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), n) == 0
+        fn()
+        ids = (ctypes.c_int32 * n)()
+        count = lib.snapkv_trace_end(ids, n)
+        torch.cuda.synchronize()
+    finally:
+        for i in range(2 * n):
+            hip.hipEventDestroy(ev[i])
+    return [int(ids[i]) for i in range(min(count, n))]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[c[0] for c in PACKED])
+def test_fused_packed_iterations(case):
+    name, lengths, Hq, Hkv, d, dt, w, kp, ratio, budget, n_plant = case
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget,
+                      n_plant=n_plant, name=name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    snap = _snap()
+    q, K = to_torch(x["q_obs"]), to_torch(x["K"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget)
+    ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], **kw))
+    assert 1 in ids and 2 not in ids, "expected the fused scoring kernel, launched %s" % ids
+    run_and_check(wl, inputs=x)
 
 
 # Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
