@@ -154,6 +154,14 @@ __device__ inline int packed_item(const ObsParams &p, int u, int C, int slab_key
 
 __device__ inline float neg_inf() { return -__builtin_huge_valf(); }
 
+// The value x, which the compiler may no longer assume equal to any earlier expression:
+// lane indices derived from it after the key stream are recomputed there (a few ALU ops)
+// instead of being kept live through the stream, where every VGPR holds logits.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // Key loads: non-temporal when every key is read once, cached when the row chunks of a
 // slab read it again.
 template <bool KEEP>
@@ -435,41 +443,46 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
 
         if constexpr (MODE == kFused) {
             // All slabs of the segment publish, then meet.  Every slab publishes before it
-            // waits, and a segment never has more slabs than resident workgroups, so the
-            // wait ends; a poll limit turns a device that did not keep the grid resident
-            // (another process filling the CUs) into an error bit instead of a hang.
-            // Each wave's device-coherent stores complete (vmcnt 0) before the workgroup
-            // barrier, so the arrival below is ordered after every published row stat.
-            // The segment's two counters (arrivals, departures) start at zero; the last
-            // workgroup to depart sets both back to zero, so the next launch finds them
-            // zero without a clearing pass.  An arrival that finds the count already at
-            // the segment's size means the workspace was not zero-filled (error bit 1).
+            // waits, and a segment never has more slabs than resident workgroups (and lies in
+            // one grid iteration), so the wait ends; a poll limit turns a device that did not
+            // keep the grid resident (another process filling the CUs) into an error bit
+            // instead of a hang.  Each wave's device-coherent stores complete (vmcnt 0) before
+            // the workgroup barrier, so the arrival below is ordered after every published
+            // row stat.  The (segment, chunk) arrival count is zero when a launch starts; the
+            // last arrival sets it back to zero at once, which also releases the others: a
+            // workgroup that arrived with `before` earlier arrivals sees the count in
+            // (before, ns] until then, and at or below `before` after.  So the next launch
+            // finds it at zero without a clearing pass.  An arrival that finds the count
+            // already at the segment's size means the workspace was not zero-filled (error
+            // bit 1).
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (tid == 0) {
-                uint32_t *arrived = &p.counters[seg * kCounterStride];
+                uint32_t *const arrived = &p.counters[seg * kCounterStride];
+                const uint32_t ns = (uint32_t)sp.ns;
                 const uint32_t before = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (before >= (uint32_t)sp.ns) __hip_atomic_fetch_or(p.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                uint32_t spins = 0;  // the last arrival knows every slab has published
-                while (before + 1 < (uint32_t)sp.ns &&
-                       __hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)sp.ns) {
-                    __builtin_amdgcn_s_sleep(8);
-                    if (++spins > p.spin_limit) {
-                        __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                }
-                const uint32_t left = __hip_atomic_fetch_add(arrived + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (left == (uint32_t)sp.ns - 1) {
+                if (before >= ns) __hip_atomic_fetch_or(p.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (before + 1 == ns) {
                     __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(arrived + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    uint32_t spins = 0;
+                    for (;;) {
+                        const uint32_t now = __hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (now == ns || now <= before) break;
+                        __builtin_amdgcn_s_sleep(8);
+                        if (++spins > p.spin_limit) {
+                            __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            break;
+                        }
+                    }
                 }
             }
             __syncthreads();
             asm volatile("" ::: "memory");
             // Merge the segment's row stats; factor for this slab's resident weights.
             constexpr int TPR = NT / MROWS;  // threads per row (power of two)
-            const int row = tid / TPR, sub = tid - (tid / TPR) * TPR;
+            const int tid_m = opaque(tid);
+            const int row = tid_m / TPR, sub = tid_m - (tid_m / TPR) * TPR;
             // A thread's slabs are read kMergeBatch at a time, all loads in flight together (an
             // index past the segment re-reads its last slab and is then ignored): long segments
             // cost a few round trips, not one per slab.
@@ -537,9 +550,13 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
         // Votes: weight * row factor, summed over this wave's rows, the four row groups of
         // the MFMA layout, then the row waves.
         {
+            const int tid_v = opaque(tid);
+            const int lane_v = tid_v & 63, wk_v = (tid_v >> 6) % WK;
+            const int grp_v = lane_v >> 4;
+            const int jl = key0 + wk_v * 16 + (lane_v & 15);  // tile_key(ct) + n16 = jl + ct * WK * 16
             float f[RTW][4];
             static_for<RTW>([&](auto rt) {
-                static_for<4>([&](auto i) { f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp + i]; });
+                static_for<4>([&](auto i) { f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp_v + i]; });
             });
             float *vout = p.votes + chunk * p.vplane + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
             static_for<CTW>([&](auto ct) {
@@ -549,8 +566,8 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 });
                 v = cross_row_sum4(v);
                 // this wave holds every row: its 16 lanes of group 0 store the tile's votes
-                const int j = tile_key(ct) + n16;
-                if (grp == 0 && j < P) vout[j] = v;
+                const int j = jl + ct() * WK * 16;
+                if (grp_v == 0 && j < P) vout[j] = v;
             });
             __syncthreads();
         }

@@ -50,7 +50,7 @@ struct ObsParams {
     float *votes;               // [H_kv][sum_P]
     float2 *partial;            // [slabs][M_pad]: (max of raw logits, sum of exp2((s-max)*c))
     const float2 *merged;       // [segments][M_pad]: merged (max, sum) for kVotes
-    uint32_t *counters;         // [segments * kCounterStride]: arrivals, departures (kFused)
+    uint32_t *counters;         // [segments * kCounterStride]: arrival count (kFused)
     uint32_t *err;              // error word (bit 0: a barrier wait gave up; bit 1: counters not zero)
     int64_t head_stride;        // elements
     int64_t token_stride;       // elements
