@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
     __shared__ float sh_m[WK][MROWS];
     __shared__ float sh_l[WK][MROWS];
     __shared__ float sh_rowm[MROWS];
-    __shared__ float sh_f[MROWS];
+    __shared__ float sh_f[MODE == kFused ? WK : 1][MROWS];  // votes factor per (wave, row)
     __shared__ int sh_wrow[kMaxRows];  // window row (row % L_obs) of each query row, for the causal mask
 
     const int tid = threadIdx.x;
@@ -365,34 +365,16 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
         }
 
         if constexpr (MODE == kFused || MODE == kStats) {
-            // Row max over the slab.
-            float mrow[RTW][4];
+            // Each wave: row max over its own tiles, exponentials against that max, row sums.
+            // No wave waits for the others before its exponentials, so the faster waves do
+            // theirs while the slowest is still streaming; the waves' (max, sum) pairs meet in
+            // LDS once, and the votes later scale each wave's weights by its own factor.
+            float mrow[RTW][4], lrow[RTW][4];
             static_for<RTW>([&](auto rt) {
                 static_for<4>([&](auto i) {
                     float m = S[rt][0][i()];
                     static_for<CTW - 1>([&](auto ct) { m = fmaxf(m, S[rt][ct + 1][i()]); });
                     mrow[rt][i] = row16_max(m);
-                });
-            });
-            if constexpr (WK > 1) {
-                if (n16 == 0)
-                    static_for<RTW>([&](auto rt) {
-                        static_for<4>([&](auto i) { sh_m[wk][(wr * RTW + rt) * 16 + 4 * grp + i] = mrow[rt][i]; });
-                    });
-                __syncthreads();
-                static_for<RTW>([&](auto rt) {
-                    static_for<4>([&](auto i) {
-                        const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                        float m = sh_m[0][row];
-                        static_for<WK - 1>([&](auto k2) { m = fmaxf(m, sh_m[k2 + 1][row]); });
-                        mrow[rt][i] = m;
-                    });
-                });
-            }
-            // Exponentials in place and row sums.
-            float lrow[RTW][4];
-            static_for<RTW>([&](auto rt) {
-                static_for<4>([&](auto i) {
                     const float sh = mrow[rt][i] == neg_inf() ? 0.f : mrow[rt][i] * c;
                     float l = 0.f;
                     static_for<CTW>([&](auto ct) {
@@ -403,39 +385,35 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                     lrow[rt][i] = row16_sum(l);
                 });
             });
-            if constexpr (WK > 1) {
-                if (n16 == 0)
-                    static_for<RTW>([&](auto rt) {
-                        static_for<4>([&](auto i) { sh_l[wk][(wr * RTW + rt) * 16 + 4 * grp + i] = lrow[rt][i]; });
-                    });
-                __syncthreads();
+            if (n16 == 0)
                 static_for<RTW>([&](auto rt) {
                     static_for<4>([&](auto i) {
                         const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                        float l = sh_l[0][row];
-                        static_for<WK - 1>([&](auto k2) { l += sh_l[k2 + 1][row]; });
-                        lrow[rt][i] = l;
+                        sh_m[wk][row] = mrow[rt][i];
+                        sh_l[wk][row] = lrow[rt][i];
                     });
                 });
-            }
-            if (wk == 0 && n16 == 0) {
-                static_for<RTW>([&](auto rt) {
-                    static_for<4>([&](auto i) {
-                        const int row = (wr * RTW + rt) * 16 + 4 * grp + i;
-                        if (row < Mc) {
-                            // device-coherent store (bypasses the per-XCD L2): the barrier below
-                            // needs no cache write-back
-                            const float2 st = make_float2(mrow[rt][i], lrow[rt][i]);
-                            __hip_atomic_store((uint64_t *)&p.partial[(int64_t)v * p.M_pad + row],
-                                               __builtin_bit_cast(uint64_t, st), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        sh_rowm[row] = mrow[rt][i];
+            __syncthreads();
+            // The slab's (max, sum) per row, merged over the waves by one thread per row and
+            // published with a device-coherent store (bypasses the per-XCD L2: the barrier
+            // below needs no cache write-back).
+            if (tid < MROWS) {
+                const int row = tid;
+                float m = sh_m[0][row];
+                static_for<WK - 1>([&](auto k2) { m = fmaxf(m, sh_m[k2 + 1][row]); });
+                float l = 0.f;
+                if (m != neg_inf())
+                    static_for<WK>([&](auto k2) {
+                        const float mk = sh_m[k2][row];
+                        if (mk != neg_inf()) l = fmaf(sh_l[k2][row], fast_exp2((mk - m) * c), l);
                     });
-                });
+                if (row < Mc) {
+                    const float2 st = make_float2(m, l);
+                    __hip_atomic_store((uint64_t *)&p.partial[(int64_t)v * p.M_pad + row],
+                                       __builtin_bit_cast(uint64_t, st), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
         }
-
         if constexpr (MODE == kStats) {
             __syncthreads();
             continue;
@@ -512,8 +490,12 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                 merge_stats(mm, ll, m2, l2, c);
             }
             if (sub == 0) {
-                const float rm = sh_rowm[row];
-                sh_f[row] = (row < Mc && rm != neg_inf() && ll > 0.f) ? fast_exp2((rm - mm) * c) / ll : 0.f;
+                // each wave's weights are relative to its own row max
+                const float inv = (row < Mc && ll > 0.f) ? 1.f / ll : 0.f;
+                static_for<WK>([&](auto k2) {
+                    const float mk = sh_m[k2][row];
+                    sh_f[k2][row] = (inv > 0.f && mk != neg_inf()) ? fast_exp2((mk - mm) * c) * inv : 0.f;
+                });
             }
             __syncthreads();
         }
@@ -529,13 +511,13 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
                         lv = p.lse[((int64_t)p.rt.qi[sp.r] * p.Hq + (int64_t)sp.g * p.G) * p.w + cbase + row];
                     const bool ok = lv != neg_inf();
                     sh_rowm[row] = ok ? lv * p.lse_scale : 0.f;
-                    sh_f[row] = ok ? 1.f : 0.f;
+                    sh_f[0][row] = ok ? 1.f : 0.f;
                 } else {
                     float2 mg = make_float2(0.f, 0.f);
                     if (row < Mc) mg = p.merged[(int64_t)seg * p.M_pad + row];
                     const bool ok = row < Mc && mg.x != neg_inf() && mg.y > 0.f;
                     sh_rowm[row] = ok ? mg.x : 0.f;
-                    sh_f[row] = ok ? 1.f / mg.y : 0.f;
+                    sh_f[0][row] = ok ? 1.f / mg.y : 0.f;
                 }
             }
             __syncthreads();
@@ -556,7 +538,7 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             const int jl = key0 + wk_v * 16 + (lane_v & 15);  // tile_key(ct) + n16 = jl + ct * WK * 16
             float f[RTW][4];
             static_for<RTW>([&](auto rt) {
-                static_for<4>([&](auto i) { f[rt][i] = sh_f[(wr * RTW + rt) * 16 + 4 * grp_v + i]; });
+                static_for<4>([&](auto i) { f[rt][i] = sh_f[MODE == kFused ? wk_v : 0][(wr * RTW + rt) * 16 + 4 * grp_v + i]; });
             });
             float *vout = p.votes + chunk * p.vplane + (int64_t)sp.g * p.sum_P + p.rt.pfx0[sp.r];
             static_for<CTW>([&](auto ct) {
