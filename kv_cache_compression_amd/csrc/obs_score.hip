@@ -24,14 +24,15 @@
 //     B, so every dot product is unchanged.
 //   * kFused keeps the slab's logits in registers: per-row max and sum of exponentials
 //     over the slab are published, the slabs of a segment meet at a counter barrier
-//     (the grid never exceeds what the device keeps resident and a segment never has
-//     more slabs than the grid, so every slab of a segment is running), each slab
+//     (the grid never exceeds what the device keeps resident, a segment never has more
+//     slabs than the grid, and with several grid iterations the items are laid out so
+//     that no segment crosses one, so every slab of a segment is running), each slab
 //     merges the segment's row stats and turns its resident logits into votes.  K is
 //     read from HBM once.  Row stats and counters move through device-coherent (sc1)
 //     atomic loads and stores, so the barrier needs no L2 write-back or invalidate.
-//   * kStats / kVotes are the two-pass path for segments with more slabs than fit on
-//     the chip at once: first pass publishes stats, merge_kernel combines them, second
-//     pass recomputes the logits and writes votes.
+//   * kStats / kVotes are the two-pass path (segments longer than the grid, layouts that
+//     would leave many slots idle, or on request): first pass publishes stats,
+//     merge_kernel combines them, second pass recomputes the logits and writes votes.
 // Exponentials are base 2: s*log2(e)/sqrt(d) with the scale folded into one FMA.
 #include <type_traits>
 
