@@ -415,7 +415,7 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
         // (which reads K twice but keeps every workgroup busy).
         bool fused = !(p.flags & SNAPKV_FLAG_TWO_PASS) && resident > 0 && (int64_t)gr.max_ns * C <= resident;
         const int grid = items < resident ? (int)items : resident;
-        if (fused && items > resident) {
+        if (!lse && fused && items > resident) {
             op.pack_grid = resident;
             const int64_t slots = pack_segments(p, gr, resident, op.vb);
             if (slots > 0x7fffffff) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
