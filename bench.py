@@ -369,23 +369,33 @@ def main():
         a_cur = torch.rand((Hkv, spec0.sum_P), device=dev) * 0.1
         counts = torch.empty((wl.batch, Hkv, 2), dtype=torch.int32, device=dev)
         n_hit = 20
-        ev_h = [hip.events(2) for _ in range(n_hit)]
+        # one launch per call, or two (the counts' clearing kernel, then the tiles) when a
+        # segment spans several tiles
+        ev_h = [hip.events(4) for _ in range(n_hit)]
+        n_launch = []
         with torch.cuda.stream(stream):
             for i in range(n_hit + 3):
                 if i >= 3:
-                    lib.snapkv_trace_begin(ctypes.cast(ev_h[i - 3], ctypes.POINTER(ctypes.c_void_p)), 1)
+                    lib.snapkv_trace_begin(ctypes.cast(ev_h[i - 3], ctypes.POINTER(ctypes.c_void_p)), 2)
                 st = lib.snapkv_hit_rate(ctypes.byref(spec0.pb), ctypes.c_void_p(a_cur.data_ptr()),
                                          ctypes.c_void_p(idx.data_ptr()), ctypes.c_double(0.05),
                                          ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
                 if i >= 3:
-                    ids1 = (ctypes.c_int32 * 1)()
-                    lib.snapkv_trace_end(ids1, 1)
+                    ids2 = (ctypes.c_int32 * 2)()
+                    n_launch.append(lib.snapkv_trace_end(ids2, 2))
+                    if n_launch[-1] not in (1, 2):
+                        raise RuntimeError("snapkv_hit_rate: expected one or two launches")
                 if st != 0:
                     raise RuntimeError("snapkv_hit_rate: %s" % lib.snapkv_last_error().decode())
         torch.cuda.synchronize()
-        us = 1e3 * sum(hip.elapsed_ms(ev_h[i][0], ev_h[i][1]) for i in range(n_hit)) / n_hit
+        two = n_launch[0] == 2
+        clear_us = 1e3 * sum(hip.elapsed_ms(ev_h[i][0], ev_h[i][1]) for i in range(n_hit)) / n_hit if two else 0.0
+        j = 2 if two else 0
+        tiles_us = 1e3 * sum(hip.elapsed_ms(ev_h[i][j], ev_h[i][j + 1]) for i in range(n_hit)) / n_hit
+        us = clear_us + tiles_us
         hb = 4 * Hkv * spec0.sum_P + 4 * Hkv * spec0.sum_k + 8 * wl.batch * Hkv
-        hit = {"avg_launch_us": round(us, 3), "alg_bytes": hb, "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
+        hit = {"avg_launch_us": round(us, 3), "clear_us": round(clear_us, 3), "tiles_us": round(tiles_us, 3),
+               "alg_bytes": hb, "GB/s": round(hb / (us * 1e-6) / 1e9, 1)}
 
     # ---- decode attention over the compressed cache (optional) ------------------------------
     dec = None

@@ -250,7 +250,8 @@ typedef enum {
     SNAPKV_K_SELECT_TILES = 9, /* topk_select of segments longer than 32768 positions (4 phases) */
     SNAPKV_K_HIT_RATE = 10,    /* snapkv_hit_rate */
     SNAPKV_K_DECODE = 11,      /* snapkv_decode: split-K partials */
-    SNAPKV_K_DECODE_COMBINE = 12 /* snapkv_decode: merge of the splits */
+    SNAPKV_K_DECODE_COMBINE = 12, /* snapkv_decode: merge of the splits */
+    SNAPKV_K_HIT_CLEAR = 13       /* snapkv_hit_rate: zeroes the counts its tiles add to */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -753,6 +753,16 @@ int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t 
     DevInfo di;
     st = device_info(&di);
     if (st) return st;
+    // the tiles of a segment longer than one tile add their counts, so they start from zero
+    // (a segment of one tile stores them)
+    if (p.max_P > hit_tile_positions()) {
+        ClearParams cp;
+        cp.data = counts;
+        cp.n = p.B * p.Hkv * 2;
+        st = launch(SNAPKV_K_HIT_CLEAR, hit_clear(), dim3((unsigned)((cp.n + 255) / 256)), dim3(256), &cp,
+                    (hipStream_t)stream);
+        if (st) return finish(st);
+    }
     for (const Group &gr : p.groups) {
         HitParams hp;
         memset(&hp, 0, sizeof hp);
@@ -765,7 +775,10 @@ int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t 
         hp.w = p.w;
         hp.Hkv = p.Hkv;
         hp.rt = gr.rt;
-        st = launch(SNAPKV_K_HIT_RATE, hit_kernel(), dim3(gr.rt.n * p.Hkv), dim3(select_threads()), &hp,
+        // at least one tile: the first tile of an empty prefix writes its zero counts
+        const unsigned tiles =
+            gr.max_P > 0 ? (unsigned)((gr.max_P + hit_tile_positions() - 1) / hit_tile_positions()) : 1u;
+        st = launch(SNAPKV_K_HIT_RATE, hit_kernel(), dim3(tiles, gr.rt.n * p.Hkv), dim3(select_threads()), &hp,
                     (hipStream_t)stream);
         if (st) return finish(st);
     }
@@ -929,6 +942,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_HIT_RATE: return "hit_rate";
         case SNAPKV_K_DECODE: return "decode_attention";
         case SNAPKV_K_DECODE_COMBINE: return "decode_combine";
+        case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
         default: return "unknown";
     }
 }

@@ -660,12 +660,15 @@ __global__ void __launch_bounds__(kSelThreads) topk_select_kernel(const SelectPa
 const void *select_kernel() { return (const void *)&topk_select_kernel; }
 
 // ---- hit rate -----------------------------------------------------------------------------------
-// One 1024-thread workgroup per (request, KV head).  The kept positions of up to kHitSpan
-// positions at a time (a contiguous run of the ascending idx, found by binary search) are
-// marked in an LDS bitmap with one coalesced pass over idx; then the attention values of the
-// span stream through with 16 loads in flight per thread.  The threshold test runs in fp64
-// on the fp32 attention values.
-constexpr int kHitSpan = 1 << 20;
+// grid: (tiles of kHitTile positions, (request, KV head) segments of the group), 1024 threads.
+// A workgroup marks the kept positions of its tile in an LDS bitmap (its run of the ascending
+// idx: with k small against the tile, one coalesced pass over the segment's idx; else the run
+// found by binary search), streams the tile's attention values with 16 loads in flight per
+// thread, and adds its integer counts to the segment's, which hit_clear_kernel zeroed just
+// before (integer sums: the result does not depend on the order of the adds); a segment of
+// one tile stores its counts directly.  The threshold test runs in fp64 on the fp32
+// attention values.
+constexpr int kHitTile = 32768;
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int x) {
     int lo = 0, hi = n;
@@ -677,45 +680,56 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t *a, int n, int x) {
     return lo;
 }
 
+__global__ void __launch_bounds__(256) hit_clear_kernel(const ClearParams p) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < p.n) p.data[i] = 0u;
+}
+
 __global__ void __launch_bounds__(kSelThreads) hit_rate_kernel(const HitParams p) {
-    __shared__ uint32_t bits[kHitSpan / 32];
+    __shared__ uint32_t bits[kHitTile / 32];
     __shared__ int range[2];
     __shared__ uint32_t wsum[2][kSelWaves];
-    const int seg = blockIdx.x;
+    const int seg = blockIdx.y;
     const int r = seg / p.Hkv, g = seg - (seg / p.Hkv) * p.Hkv;
     const int P = p.rt.L[r] - p.w;
+    const int c0 = blockIdx.x * kHitTile;
+    if (c0 >= P) {  // whole workgroup: this segment is shorter than the longest
+        if (c0 == 0 && threadIdx.x == 0) {  // an empty prefix counts nothing
+            uint32_t *out = p.counts + ((int64_t)p.rt.qi[r] * p.Hkv + g) * 2;
+            out[0] = 0u;
+            out[1] = 0u;
+        }
+        return;
+    }
+    const int span = P - c0 < kHitTile ? P - c0 : kHitTile;
     const int k = p.rt.k[r];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float *a = p.a_cur + (int64_t)g * p.sum_P + p.rt.pfx0[r];
+    const float *a = p.a_cur + (int64_t)g * p.sum_P + p.rt.pfx0[r] + c0;
     const int32_t *ix = p.idx + (int64_t)g * p.sum_k + p.rt.k0[r];
-    uint32_t hits = 0, above = 0;
-    for (int c0 = 0; c0 < P; c0 += kHitSpan) {
-        const int span = P - c0 < kHitSpan ? P - c0 : kHitSpan;
-        for (int i = tid; i < (span + 31) / 32; i += kSelThreads) bits[i] = 0;
-        if (tid < 2) range[tid] = c0 == 0 && P <= kHitSpan ? (tid ? k : 0) : lower_bound_i32(ix, k, c0 + tid * kHitSpan);
-        __syncthreads();
-        for (int t = range[0] + tid; t < range[1]; t += kSelThreads) {
-            const int j = ix[t] - c0;  // in [0, span) for an ascending idx
-            if (j >= 0 && j < span) atomicOr(&bits[j >> 5], 1u << (j & 31));
-        }
-        __syncthreads();
-        for (int b0 = 0; b0 < span; b0 += 16 * kSelThreads) {
-            float v[16];
-            static_for<16>([&](auto i) {
-                const int jl = b0 + i() * kSelThreads + tid;
-                v[i()] = jl < span ? a[c0 + jl] : 0.f;
-            });
-            static_for<16>([&](auto i) {
-                const int jl = b0 + i() * kSelThreads + tid;
-                if (jl < span && (double)v[i()] > p.theta) {
-                    ++above;
-                    hits += (bits[jl >> 5] >> (jl & 31)) & 1u;
-                }
-            });
-        }
-        __syncthreads();
+    for (int i = tid; i < kHitTile / 32; i += kSelThreads) bits[i] = 0;
+    if (tid < 2) range[tid] = k <= 4 * kHitTile ? (tid ? k : 0) : lower_bound_i32(ix, k, c0 + tid * span);
+    __syncthreads();
+    for (int t = range[0] + tid; t < range[1]; t += kSelThreads) {
+        const int j = ix[t] - c0;
+        if (j >= 0 && j < span) atomicOr(&bits[j >> 5], 1u << (j & 31));
     }
-    // workgroup sums (exact integers)
+    __syncthreads();
+    uint32_t hits = 0, above = 0;
+    for (int b0 = 0; b0 < span; b0 += 16 * kSelThreads) {
+        float v[16];
+        static_for<16>([&](auto i) {
+            const int jl = b0 + i() * kSelThreads + tid;
+            v[i()] = jl < span ? a[jl] : 0.f;
+        });
+        static_for<16>([&](auto i) {
+            const int jl = b0 + i() * kSelThreads + tid;
+            if (jl < span && (double)v[i()] > p.theta) {
+                ++above;
+                hits += (bits[jl >> 5] >> (jl & 31)) & 1u;
+            }
+        });
+    }
+    // workgroup sums (exact integers), added to the segment's counts
     hits = wave_incl_scan(hits);
     above = wave_incl_scan(above);
     if (lane == 63) {
@@ -729,10 +743,18 @@ __global__ void __launch_bounds__(kSelThreads) hit_rate_kernel(const HitParams p
             h += wsum[0][w2];
             n += wsum[1][w2];
         }
-        p.counts[((int64_t)p.rt.qi[r] * p.Hkv + g) * 2 + 0] = h;
-        p.counts[((int64_t)p.rt.qi[r] * p.Hkv + g) * 2 + 1] = n;
+        uint32_t *out = p.counts + ((int64_t)p.rt.qi[r] * p.Hkv + g) * 2;
+        if (P <= kHitTile) {  // the segment's only tile: its counts are the segment's
+            out[0] = h;
+            out[1] = n;
+        } else {
+            if (h) atomicAdd(out, h);
+            if (n) atomicAdd(out + 1, n);
+        }
     }
 }
+const void *hit_clear() { return (const void *)&hit_clear_kernel; }
+int hit_tile_positions() { return kHitTile; }
 const void *hit_kernel() { return (const void *)&hit_rate_kernel; }
 
 // ---- gather -----------------------------------------------------------------------------------

@@ -166,6 +166,12 @@ struct HitParams {
     ReqTable rt;
 };
 const void *hit_kernel();
+struct ClearParams {
+    uint32_t *data;
+    int32_t n;
+};
+const void *hit_clear();       // zeroes data[0, n); grid ceil(n / 256) x 256 threads
+int hit_tile_positions();      // positions per hit_rate workgroup (grid x = tiles of the longest)
 
 struct DecodeParams {
     const void *q;              // [B][H_q][d]

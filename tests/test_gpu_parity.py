@@ -251,7 +251,8 @@ def test_lse_fed_single_pass(case):
         check_gather(x["K"][g, t0:t1], K_out[g, int(spec.cu_out[r]):int(spec.cu_out[r + 1])], ig, P, w, tag + " gather")
 
 
-@pytest.mark.parametrize("lengths", [[3000, 40, 1200], [70000]], ids=["short", "long"])
+@pytest.mark.parametrize("lengths", [[3000, 40, 1200], [70000], [3000, 32, 70000]],
+                         ids=["short", "long", "mixed_with_empty_prefix"])
 def test_hit_rate_matches_oracle(lengths):
     """snapkv_hit_rate counts per (request, KV head) give the oracle's Hit Rate exactly: random
     attention with values exactly at theta (as float32) and next to it, and a selection from
@@ -292,8 +293,7 @@ def test_hit_rate_matches_oracle(lengths):
 
 
 def test_hit_rate_beyond_one_bitmap_span():
-    """A segment of more than 2^20 positions is counted span by span (a kept position
-    near every span edge)."""
+    """A segment of more than 2^20 positions (33 tiles; kept positions near 2^20)."""
     snap = _snap()
     w, Hkv, P = 8, 1, (1 << 20) + 5000
     cu = np.array([0, P + w], np.int32)
@@ -309,6 +309,30 @@ def test_hit_rate_beyond_one_bitmap_span():
     a = (rng.random((Hkv, P)) * 0.1).astype(np.float32)
     counts = snap.hit_rate_counts(torch.from_numpy(a).cuda(), idx, q, K, cu, obs_window=w, pool_kernel=7,
                                   budget=4000, theta=0.05)
+    torch.cuda.synchronize()
+    hits, above = (int(v) for v in counts.cpu().numpy().view(np.uint32)[0, 0])
+    mask = np.zeros(P, np.uint8)
+    mask[keep] = 1
+    assert above == int(np.sum(a[0].astype(np.float64) > 0.05))
+    assert hits / above == oracle.hit_rate(a[0], mask, 0.05)
+
+
+def test_hit_rate_large_selection():
+    """k above four tiles of positions: each tile finds its run of the ascending idx by
+    binary search (kept positions on both sides of every tile edge)."""
+    snap = _snap()
+    w, Hkv, P, k, tile = 8, 1, 300000, 200000, 32768
+    cu = np.array([0, P + w], np.int32)
+    q = torch.zeros((1, 1, w, 64), dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros((Hkv, P + w, 64), dtype=torch.bfloat16, device="cuda")
+    rng = np.random.default_rng(13)
+    edges = np.array([e + o for e in range(tile, P, tile) for o in (-1, 0)] + [0, P - 1])
+    rest = np.setdiff1d(np.arange(P), edges)
+    keep = np.sort(np.concatenate([edges, rng.choice(rest, k - edges.size, replace=False)]))
+    idx = torch.from_numpy(keep.astype(np.int32)[None, :]).cuda()
+    a = (rng.random((Hkv, P)) * 0.1).astype(np.float32)
+    counts = snap.hit_rate_counts(torch.from_numpy(a).cuda(), idx, q, K, cu, obs_window=w, pool_kernel=7,
+                                  budget=k, theta=0.05)
     torch.cuda.synchronize()
     hits, above = (int(v) for v in counts.cpu().numpy().view(np.uint32)[0, 0])
     mask = np.zeros(P, np.uint8)
