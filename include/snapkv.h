@@ -189,7 +189,8 @@ int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void 
  *   idx    : int32 [H_kv][sum_k], strictly ascending per (request, KV head), as
  *            snapkv_select writes it.
  *   theta  : threshold (the page uses 0.05); compared in double against each value.
- *   counts : out, uint32 [B][H_kv][2] = (hits, above).
+ *   counts : out, uint32 [B][H_kv][2] = (hits, above); every entry is written, so it
+ *            needs no initial value.
  * No workspace.  Errors as for the other calls (theta NaN -> SNAPKV_EINVAL).
  */
 int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t *idx, double theta, uint32_t *counts,
