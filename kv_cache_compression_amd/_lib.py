@@ -206,15 +206,44 @@ def workspace(spec: Spec, device) -> torch.Tensor:
     return ws
 
 
+def error_word_view(ws: torch.Tensor) -> torch.Tensor:
+    """The workspace's sticky error word as a 1-element int32 device view (valid once the
+    stream has reached the calls that wrote it).  Bit 0: a scoring barrier gave up waiting
+    (another kernel kept part of the scoring grid off the device); bit 1: a barrier counter
+    was not zero when a call started (the workspace was not zero-filled, or was shared by
+    calls running at the same time).  Either bit means the outputs since it was last clear
+    may be wrong; the library never clears it."""
+    return ws[:4].view(torch.int32)
+
+
+def read_error_word(ws: torch.Tensor) -> int:
+    """Waits for the current stream and returns the workspace's error word."""
+    torch.cuda.current_stream().synchronize()
+    return int(error_word_view(ws).item())
+
+
+def _raise_on_error_word(ws: torch.Tensor, where: str) -> None:
+    word = read_error_word(ws)
+    if word:
+        raise SnapKVError(EHIP, where, "workspace error word 0x%x: %s; the outputs are invalid (a device shared "
+                          "with other kernels needs two_pass=True)" % (word, "a scoring barrier gave up waiting"
+                                                                       if word & 1 else
+                                                                       "a barrier counter was not zero at the start"))
+
+
 def _check_lse(lse, q_obs):
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q_obs.shape[:3]) or not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H_q, L_obs]")
 
 
 def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-           variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None, lse=None):
+           variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None, lse=None, check_errors=True):
     """snapkv_scores (snapkv_scores_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs] is
-    given): returns (votes or None, pooled), float32 [H_kv, sum_P]."""
+    given): returns (votes or None, pooled), float32 [H_kv, sum_P].
+
+    check_errors: wait for the stream and raise SnapKVError if the workspace's error word
+    is set (see error_word_view).  With check_errors=False nothing waits; read the word
+    later with read_error_word(ws) (pass your own ws to do so)."""
     spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
     dev = K.device
     votes = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev) if want_votes else None
@@ -230,6 +259,8 @@ def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=Non
         st = load().snapkv_scores_lse(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(lse), _ptr(votes),
                                       _ptr(pooled), _ptr(ws), ctypes.c_size_t(ws.numel()), _stream())
         _check(st, "snapkv_scores_lse")
+    if check_errors:
+        _raise_on_error_word(ws, "snapkv_scores")
     return votes, pooled
 
 
@@ -264,13 +295,19 @@ def gather(K, V, idx, q_obs, cu_seqlens=None, *, obs_window=32, pool_kernel=7, r
 
 
 def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-             variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None, lse=None):
+             variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None, lse=None,
+             check_errors=True):
     """snapkv_compress (snapkv_compress_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs]
     is given): the whole path.
 
     Returns dict(K_out, V_out [H_kv, sum_out, d], idx int32 [H_kv, sum_k], cu_out int64 [B+1], k int64 [B],
-    pooled float32 [H_kv, sum_P] if want_pooled).  Defaults follow the pages' listing
-    (obs_window=32, kernel=7); exactly one of ratio and budget must be given.
+    pooled float32 [H_kv, sum_P] if want_pooled, error_word: int32 device view of the workspace's
+    error word).  Defaults follow the pages' listing (obs_window=32, kernel=7); exactly one of
+    ratio and budget must be given.
+
+    check_errors (default): wait for the stream and raise SnapKVError if the error word is set
+    (a scoring barrier gave up, or the workspace was not clean).  check_errors=False returns at
+    once; read res["error_word"] after the stream has reached the call.
     """
     spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
     if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
@@ -295,7 +332,10 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
                                         _ptr(K_out), _ptr(V_out), _ptr(idx), _ptr(pooled), _ptr(ws),
                                         ctypes.c_size_t(ws.numel()), _stream())
         _check(st, "snapkv_compress_lse")
-    res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy())
+    if check_errors:
+        _raise_on_error_word(ws, "snapkv_compress")
+    res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy(),
+               error_word=error_word_view(ws))
     if pooled is not None:
         res["pooled"] = pooled
     return res

@@ -12,7 +12,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "obs_score.hip", "select_gather.hip", "decode.hip"]
+SOURCES = ["api.hip", "obs_score.hip", "obs_inst_bf16_d128.hip", "obs_inst_bf16_d64.hip", "obs_inst_f32_d128.hip",
+           "obs_inst_f32_d64.hip", "select_gather.hip", "decode.hip"]
 LIB = os.path.join(PKG, "libsnapkv.so")
 
 HIPCC_FLAGS = [
@@ -20,7 +21,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -35,18 +35,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsnapkv)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into kv_cache_compression_amd/libsnapkv.so (always rebuilds)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _compile(src: str, obj: str) -> str:
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                                     os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError("hipcc failed on %s:\n%s" % (src, err))
+    return err
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source into kv_cache_compression_amd/libsnapkv.so (always rebuilds).
+    The sources compile in parallel (one hipcc per source), then link into one library."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = "%d" % os.getpid()
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + "." + tag + ".o") for s in SOURCES]
+    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+    try:
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            msgs = list(ex.map(_compile, SOURCES, objs))
+        tmp = LIB + ".tmp" + tag
+        res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+                             capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    if verbose:
+        for m in msgs:
+            if m.strip():
+                print(m, file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 

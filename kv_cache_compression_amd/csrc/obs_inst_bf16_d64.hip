@@ -1,0 +1,8 @@
+// obs_inst_bf16_d64.hip -- instantiations of the scoring kernel for bfloat16 keys, head size 64.
+#include "obs_score_kernel.h"
+
+namespace snapkv {
+
+const void *obs_kernel_bf16_d64(int mode, bool keep, int ctw) { return pick<__bf16, 64>(mode, keep, ctw); }
+
+}  // namespace snapkv

@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
     }
 
     const uint32_t *src = (const uint32_t *)(p.pooled + base);
-    const int lane = tid & 63, wave = tid >> 6;
+
     if (p.phase == 1) {
         const uint32_t prefix = st->prefix, mask = st->mask;
         const bool refine = st->done == 0;

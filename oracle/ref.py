@@ -137,16 +137,23 @@ def row_lse(q: np.ndarray, keys: np.ndarray, w: int, variant: int = 0) -> np.nda
     return out
 
 
-def lse_all(q_obs: np.ndarray, K: np.ndarray, cu_seqlens, w: int, variant: int = 0) -> np.ndarray:
+def lse_all(q_obs: np.ndarray, K: np.ndarray, cu_seqlens, w: int, variant: int = 0, n_threads: int = 16) -> np.ndarray:
     """row_lse for every request and query head: float64 [B, H_q, w] (q_obs [B, H_q, w, d],
-    K [H_kv, T, d]; query head h reads KV head h // G)."""
+    K [H_kv, T, d]; query head h reads KV head h // G).  The (request, head) calls run on a
+    thread pool (each call is independent)."""
+    from concurrent.futures import ThreadPoolExecutor
     B, Hq = q_obs.shape[0], q_obs.shape[1]
     G = Hq // K.shape[0]
     out = np.empty((B, Hq, w), np.float64)
-    for r in range(B):
+
+    def one(job):
+        r, h = job
         t0, t1 = int(cu_seqlens[r]), int(cu_seqlens[r + 1])
-        for h in range(Hq):
-            out[r, h] = row_lse(q_obs[r, h], K[h // G, t0:t1], w, variant)
+        out[r, h] = row_lse(q_obs[r, h], K[h // G, t0:t1], w, variant)
+
+    jobs = [(r, h) for r in range(B) for h in range(Hq)]
+    with ThreadPoolExecutor(max_workers=max(1, n_threads)) as ex:
+        list(ex.map(one, jobs))
     return out
 
 

@@ -14,8 +14,9 @@ def pytest_configure(config):
 
 def pytest_runtest_setup(item):
     # A GPU test that starts on a machine without a GPU is an error of the run, not a skip:
-    # it would otherwise pass silently without the native code.
+    # a skip would let the GPU suite look green without the native code having run.
+    # Select the CPU suite with -m "not gpu".
     if "gpu" in item.keywords:
         import torch
         if not torch.cuda.is_available():
-            pytest.skip("no GPU visible to this process")
+            pytest.fail("gpu-marked test started without a visible GPU (run the CPU suite with -m 'not gpu')")

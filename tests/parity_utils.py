@@ -1,10 +1,12 @@
 """Helpers shared by the GPU parity tests: inputs to torch, and the parity criteria.
 
 Criteria (GPU vs the fp64 oracle):
-  * votes and pooled votes: |gpu - ref| <= 1e-3 * |ref| + 1e-6 * max(ref) per
-    (request, KV head).  The relative bound is the one fixed for this path; the
-    absolute floor only admits fp32 underflow of weights a million times below the
-    segment's largest vote, far below anything top-k can pick.
+  * votes and pooled votes: |gpu - ref| <= 1e-3 * |ref| for every entry.  This is
+    the relative bound fixed for this path, with no absolute term.  The only
+    exception is a genuine fp32 underflow guard: an entry whose oracle value is
+    below UNDERFLOW (1e-30, some 2^100 below any vote these inputs produce) may
+    be anything in [0, 2 * UNDERFLOW].  check_scores returns how many entries
+    passed only by that guard and, unless told otherwise, asserts there are none.
   * selection: exactly k ascending positions in [0, P); the symmetric difference
     with the oracle's set lies inside the tie band {j : |ref_j - v*| <= 1e-3 * v*},
     v* = the oracle's k-th largest pooled vote.
@@ -19,7 +21,7 @@ import torch
 import oracle
 
 RTOL = 1e-3
-ABS_FLOOR = 1e-6
+UNDERFLOW = 1e-30
 
 
 def to_torch(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -35,17 +37,36 @@ def to_numpy_bits(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def check_scores(gpu: np.ndarray, ref: np.ndarray, what: str):
+def check_scores(gpu: np.ndarray, ref: np.ndarray, what: str, allow_underflow: bool = False) -> int:
+    """Asserts the relative bound entry by entry; returns the number of entries that
+    passed only by the underflow guard (asserted zero unless allow_underflow)."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     if ref.size == 0:
-        return
-    tol = RTOL * np.abs(ref) + ABS_FLOOR * np.max(np.abs(ref))
+        return 0
     err = np.abs(gpu - ref)
-    bad = np.nonzero(err > tol)[0]
-    assert bad.size == 0, "%s: %d of %d outside tolerance; worst j=%d gpu=%r ref=%r" % (
-        what, bad.size, ref.size, bad[np.argmax(err[bad] / tol[bad])], gpu[bad[0]], ref[bad[0]])
+    rel_ok = err <= RTOL * np.abs(ref)
+    guard_ok = (np.abs(ref) < UNDERFLOW) & (gpu >= 0.0) & (gpu <= 2 * UNDERFLOW)
+    bad = np.nonzero(~(rel_ok | guard_ok))[0]
+    if bad.size:
+        rel = err[bad] / np.maximum(np.abs(ref[bad]), 1e-300)
+        worst = bad[np.argmax(rel)]
+        raise AssertionError("%s: %d of %d outside 1e-3 relative; worst j=%d gpu=%r ref=%r rel=%.3g" % (
+            what, bad.size, ref.size, worst, gpu[worst], ref[worst], float(np.max(rel))))
+    n_guard = int(np.sum(guard_ok & ~rel_ok))
+    assert allow_underflow or n_guard == 0, "%s: %d entries pass only by the underflow guard" % (what, n_guard)
+    return n_guard
+
+
+def max_rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Largest |gpu - ref| / |ref| over entries with ref != 0 (diagnostic)."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nz = ref != 0
+    if not np.any(nz):
+        return 0.0
+    return float(np.max(np.abs(gpu[nz] - ref[nz]) / np.abs(ref[nz])))
 
 
 def check_selection(idx_gpu: np.ndarray, ref_pooled: np.ndarray, ref_idx: np.ndarray, k: int, what: str):

@@ -480,11 +480,15 @@ def test_unsupported_rows_raise():
     wl = synth.custom([600], 64, 1, 64, obs_window=17, pool_kernel=7, ratio=0.05, name="too_many_rows")
     x = synth.make_inputs(wl)
     q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
-    with pytest.raises(ValueError):
-        snap.compress(q, K, V, x["cu_seqlens"], obs_window=32, pool_kernel=7, ratio=0.05)
+    # G * L_obs = 64 * 17 = 1088 rows per KV head: past the 1024 the scoring kernels take
+    with pytest.raises(ValueError, match="1024"):
+        snap.compress(q, K, V, x["cu_seqlens"], obs_window=17, pool_kernel=7, ratio=0.05)
 
 
 # ---- the five standard workloads at full size ------------------------------------------------
+# Every (request, KV head) pair of a layer is compared with the oracle, entry by entry, in the
+# launch configuration the benchmark times.
+
 
 def test_workload1_full():
     run_and_check(synth.workload(1))
@@ -494,16 +498,52 @@ def test_workload2_full():
     run_and_check(synth.workload(2))
 
 
-def test_workload3_layers_sampled():
+def test_workload3_layers_all_heads():
+    """All 8 KV heads (each scoring 4 query heads x 64 window rows) of four of the 32 layers."""
     wl = synth.workload(3)
-    for layer in (0, wl.n_layers - 1):
-        run_and_check(wl, layer=layer, pairs=[(0, 0), (0, 5)])
+    for layer in (0, 9, 20, wl.n_layers - 1):
+        run_and_check(wl, layer=layer)
 
 
-def test_workload4_sampled_heads():
-    run_and_check(synth.workload(4), pairs=[(0, 3), (0, 30)])
+def test_workload4_all_heads():
+    run_and_check(synth.workload(4))
 
 
-def test_workload5_sampled_pairs():
-    wl = synth.workload(5)
-    run_and_check(wl, pairs=[(0, 0), (3, 7), (7, 2), (11, 4), (15, 6)])
+def test_workload5_all_pairs():
+    run_and_check(synth.workload(5))
+
+
+@pytest.mark.parametrize("n", [2, 4, 5])
+def test_lse_fed_full_size(n):
+    """snapkv_compress_lse at full size with every window row's log-sum-exp from the oracle
+    (rounded to float32): votes, pooled votes, selection and gather of every pair."""
+    snap = _snap()
+    wl = synth.workload(n)
+    _say("case lse-fed %s" % wl.name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    cu, w = x["cu_seqlens"], wl.obs_window
+    lse = torch.from_numpy(oracle.lse_all(x["q_obs"], x["K"], cu, w).astype(np.float32)).cuda()
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    kw = dict(obs_window=w, pool_kernel=wl.pool_kernel, ratio=wl.ratio, budget=wl.budget)
+    votes, pooled = snap.scores(q, K, cu, lse=lse, **kw)
+    res = snap.compress(q, K, V, cu, lse=lse, want_pooled=True, **kw)
+    torch.cuda.synchronize()
+    spec = snap.make_spec(q, K, cu, w, wl.pool_kernel, wl.ratio, wl.budget)
+    ref = oracle.compress(x["q_obs"], x["K"], x["V"], cu, w, wl.pool_kernel, ratio=wl.ratio, budget=wl.budget,
+                          with_gather=False)
+    votes, pooled_c = votes.cpu().numpy(), res["pooled"].cpu().numpy()
+    np.testing.assert_array_equal(pooled.cpu().numpy(), pooled_c)
+    idx = res["idx"].cpu().numpy()
+    K_out = to_numpy_bits(res["K_out"])
+    for (r, g), rr in sorted(ref.items()):
+        t0, t1 = int(cu[r]), int(cu[r + 1])
+        P, k = t1 - t0 - w, rr["k"]
+        tag = "%s lse r=%d g=%d" % (wl.name, r, g)
+        cols = slice(int(spec.cu_pfx[r]), int(spec.cu_pfx[r + 1]))
+        check_scores(votes[g, cols], rr["votes"], tag + " votes")
+        check_scores(pooled_c[g, cols], rr["pooled"], tag + " pooled")
+        ig = idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])]
+        check_selection(ig, rr["pooled"], rr["idx"], k, tag + " select")
+        check_select_exact(ig, pooled_c[g, cols], k, tag + " select-exact")
+        check_gather(x["K"][g, t0:t1], K_out[g, int(spec.cu_out[r]):int(spec.cu_out[r + 1])], ig, P, w,
+                     tag + " gather")
