@@ -180,6 +180,25 @@ int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void 
                         void *stream);
 
 /*
+ * snapkv_compress_noalloc -- snapkv_compress for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * takes no workspace: its workspace is a device array of SNAPKV_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per device, which the library holds until the process ends.  The call
+ * itself allocates nothing; the caller still provides every input and output.
+ *   q_obs, K, V, K_out, V_out, idx, pooled : as for snapkv_compress.
+ *   error_word : out, device uint32 (4-byte aligned) or NULL: receives the call's error bits
+ *                (the same bits as the workspace error word described under snapkv_plan),
+ *                which the call then clears in its array.
+ * A problem whose snapkv_plan ws_bytes exceeds SNAPKV_NOALLOC_SCRATCH_BYTES returns
+ * SNAPKV_EWORKSPACE before any launch.  The first call on a device zero-fills the array on
+ * `stream`.  Every call on a device shares that device's array: calls that overlap in time on
+ * one device (other streams, other threads) race and give wrong results; order them.
+ */
+#define SNAPKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int snapkv_compress_noalloc(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
+                            void *V_out, int32_t *idx, float *pooled, uint32_t *error_word, void *stream);
+
+/*
  * snapkv_hit_rate -- the Hit Rate of a selection (section Hit Rate（適中率）の定式化):
  * for each (request, KV head), `above` = the prefix positions whose attention in the
  * current generation step exceeds theta (strictly), and `hits` = those among them that
@@ -252,7 +271,8 @@ typedef enum {
     SNAPKV_K_HIT_RATE = 10,    /* snapkv_hit_rate */
     SNAPKV_K_DECODE = 11,      /* snapkv_decode: split-K partials */
     SNAPKV_K_DECODE_COMBINE = 12, /* snapkv_decode: merge of the splits */
-    SNAPKV_K_HIT_CLEAR = 13       /* snapkv_hit_rate: zeroes the counts its tiles add to */
+    SNAPKV_K_HIT_CLEAR = 13,      /* snapkv_hit_rate: zeroes the counts its tiles add to */
+    SNAPKV_K_SCRATCH_CLEAR = 14   /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

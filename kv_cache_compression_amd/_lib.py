@@ -24,7 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-           "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate", "snapkv_decode_plan", "snapkv_decode",
+           "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_compress_noalloc", "snapkv_hit_rate", "snapkv_decode_plan", "snapkv_decode",
            "snapkv_trace_begin", "snapkv_trace_end", "snapkv_kernel_name",
            "snapkv_strerror", "snapkv_last_error", "snapkv_version")
 
@@ -84,12 +84,13 @@ def load() -> ctypes.CDLL:
             lib.snapkv_compress.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_scores_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
             lib.snapkv_compress_lse.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+            lib.snapkv_compress_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.snapkv_hit_rate.argtypes = [P, vp, vp, ctypes.c_double, vp, vp]
             DP = ctypes.POINTER(DecodeProblem)
             lib.snapkv_decode_plan.argtypes = [DP, ctypes.POINTER(sz)]
             lib.snapkv_decode.argtypes = [DP, vp, vp, vp, vp, vp, sz, vp]
             for f in ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
-                      "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_hit_rate", "snapkv_decode_plan",
+                      "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_compress_noalloc", "snapkv_hit_rate", "snapkv_decode_plan",
                       "snapkv_decode"):
                 getattr(lib, f).restype = ctypes.c_int
             lib.snapkv_strerror.argtypes = [ctypes.c_int]
@@ -336,6 +337,35 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
         _raise_on_error_word(ws, "snapkv_compress")
     res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy(),
                error_word=error_word_view(ws))
+    if pooled is not None:
+        res["pooled"] = pooled
+    return res
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SNAPKV_NOALLOC_SCRATCH_BYTES
+
+
+def compress_noalloc(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
+                     variant=CAUSAL_WINDOW, two_pass=False, out=None, error_word=None):
+    """snapkv_compress_noalloc: the whole path with the library's own device scratch as the
+    workspace (the C call allocates nothing; the outputs are allocated here unless `out` gives
+    them).  error_word: optional int32 device tensor of one element that receives the call's
+    error bits.  Returns the same dict as compress() (without pooled unless out holds it)."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
+    if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
+        raise ValueError("V must match K in shape, strides and dtype")
+    dev = K.device
+    if out is None:
+        K_out = torch.empty((spec.Hkv, spec.sum_out, spec.head_dim), dtype=K.dtype, device=dev)
+        V_out = torch.empty_like(K_out)
+        idx = torch.empty((spec.Hkv, spec.sum_k), dtype=torch.int32, device=dev)
+        pooled = None
+    else:
+        K_out, V_out, idx, pooled = out["K_out"], out["V_out"], out["idx"], out.get("pooled")
+    st = load().snapkv_compress_noalloc(ctypes.byref(spec.pb), _ptr(q_obs), _ptr(K), _ptr(V), _ptr(K_out),
+                                        _ptr(V_out), _ptr(idx), _ptr(pooled), _ptr(error_word), _stream())
+    _check(st, "snapkv_compress_noalloc")
+    res = dict(K_out=K_out, V_out=V_out, idx=idx, cu_out=spec.cu_out.copy(), k=spec.k.copy())
     if pooled is not None:
         res["pooled"] = pooled
     return res

@@ -582,9 +582,12 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
     return SNAPKV_OK;
 }
 
+// err_word (optional): the call's workspace error word, which the last gather launch copies
+// to err_out (optional) and clears.
 int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, void *K_out, void *V_out,
-               hipStream_t stream) {
-    for (const Group &gr : p.groups) {
+               hipStream_t stream, uint32_t *err_word = nullptr, uint32_t *err_out = nullptr) {
+    for (size_t gi = 0; gi < p.groups.size(); ++gi) {
+        const Group &gr = p.groups[gi];
         GatherParams gp;
         memset(&gp, 0, sizeof gp);
         gp.K = K;
@@ -600,6 +603,10 @@ int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, 
         gp.esz = p.esz;
         gp.w = p.w;
         gp.Hkv = p.Hkv;
+        if (gi + 1 == p.groups.size()) {
+            gp.err_word = err_word;
+            gp.err_out = err_out;
+        }
         gp.rt = gr.rt;
         const int tile = 256 / (p.row_bytes / 16) * gather_rows_per_thread();
         int64_t blocks = (gr.out_rows + tile - 1) / tile;
@@ -608,6 +615,40 @@ int run_gather(const Plan &p, const void *K, const void *V, const int32_t *idx, 
         int st = launch(SNAPKV_K_GATHER, gather_kernel(), dim3((unsigned)blocks, p.Hkv), dim3(256), &gp, stream);
         if (st) return st;
     }
+    return SNAPKV_OK;
+}
+
+// ---- the allocation-free call's workspace: one array per device --------------------------
+// A file-scope device array stands in for the caller's workspace.  Its name is a host-side
+// stand-in in host code, so every host use goes through the address hipGetSymbolAddress
+// returns for the current device (each device holds its own copy).
+static __device__ __align__(256) unsigned char scratch[SNAPKV_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[64];
+
+// The current device's scratch address.  The first call on a device looks it up and zero-fills
+// the array on `stream` (every later call finds its barrier counters back at zero, as a
+// zero-filled workspace requires).
+int scratch_for_device(hipStream_t stream, void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SNAPKV_EHIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= 64) return fail(SNAPKV_EUNSUPPORTED, "device ordinal out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SNAPKV_EHIP, std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e));
+        ClearParams cp;
+        cp.data = (uint32_t *)ptr;
+        cp.n = (int32_t)(SNAPKV_NOALLOC_SCRATCH_BYTES / sizeof(uint32_t));
+        const int st = launch(SNAPKV_K_SCRATCH_CLEAR, hit_clear(), dim3((unsigned)((cp.n + 255) / 256)), dim3(256), &cp,
+                              stream);
+        if (st) return st;
+        g_scratch_ptr[dev] = (char *)ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return SNAPKV_OK;
 }
 
@@ -702,9 +743,10 @@ int snapkv_gather(const snapkv_problem *pb, const void *K, const void *V, const 
     return finish(run_gather(p, K, V, idx, K_out, V_out, (hipStream_t)stream));
 }
 
+// ws == nullptr: the allocation-free call, whose workspace is the device's scratch array.
 static int compress_impl(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, const float *lse,
                          bool need_lse, void *K_out, void *V_out, int32_t *idx, float *pooled, void *ws,
-                         size_t ws_bytes, void *stream) {
+                         size_t ws_bytes, void *stream, bool noalloc = false, uint32_t *err_out = nullptr) {
     Plan p;
     int st = make_plan(pb, &p);
     if (!st) st = check_ptr(q_obs, "q_obs");
@@ -715,10 +757,18 @@ static int compress_impl(const snapkv_problem *pb, const void *q_obs, const void
     if (!st) st = check_ptr(V_out, "V_out");
     if (!st) st = check_opt_ptr(idx, "idx");
     if (!st) st = check_opt_ptr(pooled, "pooled");
-    if (!st) st = check_ws(p, ws, ws_bytes);
+    if (!st && noalloc && err_out && ((uintptr_t)err_out & 3u)) st = fail(SNAPKV_EINVAL, "error_word must be 4-byte aligned");
+    if (!st && noalloc && p.ws_bytes > SNAPKV_NOALLOC_SCRATCH_BYTES)
+        st = fail(SNAPKV_EWORKSPACE, "problem needs " + std::to_string(p.ws_bytes) + " bytes of scratch; the "
+                  "allocation-free call holds " + std::to_string((size_t)SNAPKV_NOALLOC_SCRATCH_BYTES));
+    if (!st && !noalloc) st = check_ws(p, ws, ws_bytes);
     if (st) return st;
-    char *w = (char *)ws;
     hipStream_t s = (hipStream_t)stream;
+    if (noalloc) {
+        st = scratch_for_device(s, &ws);
+        if (st) return st;
+    }
+    char *w = (char *)ws;
     float *votes = (float *)(w + p.off_votes);
     // pooled votes: the caller's buffer, or workspace when long segments need them in memory
     const bool need_pooled = p.max_P > select_lds_positions() || !select_fuses_pool(p, p.max_P);
@@ -726,7 +776,7 @@ static int compress_impl(const snapkv_problem *pb, const void *q_obs, const void
     int32_t *ix = idx ? idx : (int32_t *)(w + p.off_idx);
     st = run_scores(p, q_obs, K, lse, votes, nullptr, false, w, s);
     if (!st) st = run_select(p, votes, pl, ix, w, s);
-    if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s);
+    if (!st) st = run_gather(p, K, V, ix, K_out, V_out, s, noalloc ? (uint32_t *)(w + p.off_err) : nullptr, err_out);
     return finish(st);
 }
 
@@ -739,6 +789,12 @@ int snapkv_compress_lse(const snapkv_problem *pb, const void *q_obs, const void 
                         void *K_out, void *V_out, int32_t *idx, float *pooled, void *ws, size_t ws_bytes,
                         void *stream) {
     return compress_impl(pb, q_obs, K, V, lse, true, K_out, V_out, idx, pooled, ws, ws_bytes, stream);
+}
+
+int snapkv_compress_noalloc(const snapkv_problem *pb, const void *q_obs, const void *K, const void *V, void *K_out,
+                            void *V_out, int32_t *idx, float *pooled, uint32_t *error_word, void *stream) {
+    return compress_impl(pb, q_obs, K, V, nullptr, false, K_out, V_out, idx, pooled, nullptr, 0, stream, true,
+                         error_word);
 }
 
 int snapkv_hit_rate(const snapkv_problem *pb, const float *a_cur, const int32_t *idx, double theta, uint32_t *counts,
@@ -943,6 +999,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_DECODE: return "decode_attention";
         case SNAPKV_K_DECODE_COMBINE: return "decode_combine";
         case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
+        case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
         default: return "unknown";
     }
 }

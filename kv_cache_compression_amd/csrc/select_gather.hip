@@ -769,6 +769,13 @@ int gather_rows_per_thread() { return kGatherRows; }
 
 __global__ void __launch_bounds__(256) kv_gather_kernel(const GatherParams p) {
     const int g = blockIdx.y;
+    // The last launch of a call reports the call's error word (every earlier kernel of the
+    // call precedes it on the stream) and clears it for the next call.
+    if (p.err_word && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        const uint32_t e = *p.err_word;
+        if (p.err_out) *p.err_out = e;
+        *p.err_word = 0u;
+    }
     const int lpr = p.row_bytes >> 4;           // lanes per row
     const int rpb = 256 / lpr;                  // rows per block pass
     const int chunk = threadIdx.x % lpr;

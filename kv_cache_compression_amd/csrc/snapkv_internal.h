@@ -170,7 +170,7 @@ struct ClearParams {
     uint32_t *data;
     int32_t n;
 };
-const void *hit_clear();       // zeroes data[0, n); grid ceil(n / 256) x 256 threads
+const void *hit_clear();       // zeroes data[0, n); grid ceil(n / 256) x 256 threads (also used to clear scratch)
 int hit_tile_positions();      // positions per hit_rate workgroup (grid x = tiles of the longest)
 
 struct DecodeParams {
@@ -196,6 +196,8 @@ struct GatherParams {
     int64_t head_stride, token_stride;  // elements of the input
     int64_t sum_k, sum_out;
     int32_t row_bytes, esz, w, Hkv;
+    uint32_t *err_word;         // when set: copied to err_out (if set) and cleared by thread 0 of block (0, 0)
+    uint32_t *err_out;
     ReqTable rt;
 };
 const void *gather_kernel();
