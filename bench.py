@@ -39,7 +39,8 @@ METRIC = "prompt tokens compressed/s per layer + % peak HBM GB/s (Llama-7B shape
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD public specification
 CACHE_BYTES = 256 << 20          # MI355X Infinity Cache
 KERNEL_SOURCES = ("kv_cache_compression_amd/csrc/obs_score.hip", "kv_cache_compression_amd/csrc/obs_score_kernel.h")
-SCORING_KERNELS = ("obs_score_fused", "obs_score_stats", "obs_stats_merge", "obs_score_votes", "sum_chunks")
+SCORING_KERNELS = ("obs_score_fused", "obs_score_stream", "obs_score_stats", "obs_stats_merge", "obs_score_votes",
+                   "sum_chunks")
 
 
 def parse():
@@ -382,7 +383,7 @@ class Run:
             dom = max(scoring, key=scoring.get)
             n_l = launches.get(dom, 1.0) or 1.0
             res["dominant"] = dom
-            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_fused",
+            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_fused", "obs_score_stream",
                                                                             "obs_score_votes") else None
             res["dominant_launch_us"] = launch_us[dom]
         return res

@@ -78,6 +78,9 @@ typedef enum { SNAPKV_CAUSAL_WINDOW = 0, SNAPKV_PREFIX_ONLY = 1 } snapkv_variant
 
 /* flags */
 #define SNAPKV_FLAG_TWO_PASS 0x1u /* score with two passes over K (stats, then votes) */
+#define SNAPKV_FLAG_STREAM 0x2u   /* score with the streaming two-phase kernel (rows of 256 bytes,
+                                     G * L_obs <= 256; chosen by itself for grouped-query heads,
+                                     the lse calls and problems larger than one pass of the grid) */
 
 typedef struct {
     int32_t batch;            /* B >= 1 requests */
@@ -272,7 +275,8 @@ typedef enum {
     SNAPKV_K_DECODE = 11,      /* snapkv_decode: split-K partials */
     SNAPKV_K_DECODE_COMBINE = 12, /* snapkv_decode: merge of the splits */
     SNAPKV_K_HIT_CLEAR = 13,      /* snapkv_hit_rate: zeroes the counts its tiles add to */
-    SNAPKV_K_SCRATCH_CLEAR = 14   /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
+    SNAPKV_K_SCRATCH_CLEAR = 14,  /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
+    SNAPKV_K_OBS_STREAM = 15      /* obs_score, streaming two-phase kernel (work tickets, no barrier) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

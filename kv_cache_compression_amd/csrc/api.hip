@@ -52,10 +52,33 @@ struct Plan {
     int max_group_slabs, max_group_segs;
     int64_t max_P;
     int max_tiles;     // tiles of the longest segment (long-segment select)
+    // streaming two-phase scoring (rows of 256 bytes, G * L_obs <= 256)
+    bool st_ok;        // the streaming kernel supports this problem
+    int st_rows;       // rows per KV head the kernel covers: 32, 64, 128 or 256 (>= M)
+    int st_slab;       // keys per item
+    int64_t st_max_items;  // items of the largest group
     // workspace layout (bytes)
     size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx;
-    size_t off_long_state, off_ghist, off_cand, off_tilecnt, ws_bytes;
+    size_t off_long_state, off_ghist, off_cand, off_tilecnt;
+    size_t off_st_ticket, off_st_ctl, off_st_partial, off_st_final, ws_bytes;
 };
+
+// Streaming scoring: grid of two workgroups per CU (the plan assumes the MI355X's 256 CUs;
+// the launch uses whatever the device keeps resident).
+constexpr int kStreamNominalGrid = 512;
+
+// Items of slab keys for the requests of one group.
+static int64_t stream_items(const Plan &p, const Group &gr, int slab, int *max_ns) {
+    int64_t n = 0;
+    int mx = 0;
+    for (int i = 0; i < gr.rt.n; ++i) {
+        const int ns = (gr.rt.L[i] + slab - 1) / slab;
+        n += (int64_t)ns * p.Hkv;
+        mx = ns > mx ? ns : mx;
+    }
+    if (max_ns) *max_ns = mx;
+    return n;
+}
 
 // Groups of at most kMaxReq requests, for the slab size of p.cfg.
 static int build_groups(Plan &p, const int32_t *cu) {
@@ -140,7 +163,9 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.dtype != SNAPKV_F32 && p.dtype != SNAPKV_BF16) return fail(SNAPKV_EINVAL, "dtype must be F32 or BF16");
     if (p.variant != SNAPKV_CAUSAL_WINDOW && p.variant != SNAPKV_PREFIX_ONLY)
         return fail(SNAPKV_EINVAL, "variant must be CAUSAL_WINDOW or PREFIX_ONLY");
-    if (p.flags & ~SNAPKV_FLAG_TWO_PASS) return fail(SNAPKV_EINVAL, "unknown flag bits");
+    if (p.flags & ~(SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM)) return fail(SNAPKV_EINVAL, "unknown flag bits");
+    if ((p.flags & SNAPKV_FLAG_TWO_PASS) && (p.flags & SNAPKV_FLAG_STREAM))
+        return fail(SNAPKV_EINVAL, "SNAPKV_FLAG_TWO_PASS and SNAPKV_FLAG_STREAM exclude each other");
     if (p.mode == SNAPKV_RATIO && !(p.ratio > 0.0 && p.ratio <= 1.0))
         return fail(SNAPKV_EINVAL, "ratio must lie in (0, 1]");
     if (p.mode == SNAPKV_BUDGET && p.budget < 0) return fail(SNAPKV_EINVAL, "budget must be >= 0");
@@ -216,6 +241,29 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     for (int r = 0; r < p.B; ++r)
         if (cu[r + 1] > 0x7fffffff - 1) return fail(SNAPKV_EUNSUPPORTED, "token count exceeds int32");
 
+    // streaming kernel: 1024-key items, halved (down to 256) while a group has fewer items than
+    // the grid has workgroups
+    p.st_ok = p.row_bytes == 256 && p.M <= 256 && !(p.flags & SNAPKV_FLAG_TWO_PASS);
+    if ((p.flags & SNAPKV_FLAG_STREAM) && !p.st_ok)
+        return fail(SNAPKV_EUNSUPPORTED, "SNAPKV_FLAG_STREAM needs rows of 256 bytes and G * obs_window <= 256");
+    p.st_rows = p.M <= 32 ? 32 : p.M <= 64 ? 64 : p.M <= 128 ? 128 : 256;
+    p.st_slab = 1024;
+    p.st_max_items = 0;
+    if (p.st_ok) {
+        int64_t mx = 0;
+        for (const Group &gr : p.groups) {
+            const int64_t n = stream_items(p, gr, 1024, nullptr);
+            mx = n > mx ? n : mx;
+        }
+        const int grid = p.st_rows <= 128 ? kStreamNominalGrid : kStreamNominalGrid / 2;
+        while (p.st_slab > 256 && mx * 1024 / p.st_slab < grid) p.st_slab /= 2;
+        for (const Group &gr : p.groups) {
+            const int64_t n = stream_items(p, gr, p.st_slab, nullptr);
+            if (n > (1 << 29)) return fail(SNAPKV_EUNSUPPORTED, "problem too large");
+            p.st_max_items = n > p.st_max_items ? n : p.st_max_items;
+        }
+    }
+
     // workspace: [err (one 256-byte line)] [counters, one line per (segment, chunk)] [partial]
     // [merged] [votes planes, when rows come in several chunks] [votes] [pooled] [idx]
     const size_t C = (size_t)p.n_chunks;
@@ -246,6 +294,17 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (has_long) off = align_up(off + sizeof(uint32_t) * (size_t)p.Hkv * (size_t)p.sum_P);
     p.off_tilecnt = off;
     if (has_long) off = align_up(off + sizeof(uint32_t) * 4 * (size_t)p.max_tiles * (size_t)p.max_group_segs);
+    // streaming scoring: ticket line, three control lines per segment, per-item row stats,
+    // per-segment row shifts
+    const size_t st_rows = (size_t)p.st_rows;
+    p.off_st_ticket = off;
+    if (p.st_ok) off = align_up(off + kWsAlign);
+    p.off_st_ctl = off;
+    if (p.st_ok) off = align_up(off + sizeof(uint32_t) * 3 * kStreamSegLine * (size_t)p.max_group_segs);
+    p.off_st_partial = off;
+    if (p.st_ok) off = align_up(off + sizeof(float) * 2 * st_rows * (size_t)p.st_max_items);
+    p.off_st_final = off;
+    if (p.st_ok) off = align_up(off + sizeof(float) * st_rows * (size_t)p.max_group_segs);
     p.ws_bytes = off;
     return SNAPKV_OK;
 }
@@ -377,7 +436,67 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
     const void *kf = obs_kernel(p.dtype, p.d, cfg, kFused, keep);
     const int occ = occupancy(kf, cfg.threads());
     const int resident = occ * di.cus;
+    int st_threads = 0;
+    const void *ks = p.st_ok ? stream_kernel(p.dtype, p.st_rows, &st_threads) : nullptr;
+    const int st_grid = p.st_ok ? occupancy(ks, st_threads) * di.cus : 0;
     for (const Group &gr : p.groups) {
+        // The streaming kernel takes grouped-query heads, the caller's row stats, and problems
+        // whose logits do not fit one pass of the resident grid; the fused kernel the rest.
+        const int64_t fused_items = (int64_t)gr.n_slabs * C;
+        // Grouped-query heads and the caller's row stats go to the streaming kernel (it reads each
+        // key once for all of a group's rows); MHA stays with the fused kernel, which reads K once.
+        (void)fused_items;
+        const bool use_stream = p.st_ok && st_grid > 0 && ((p.flags & SNAPKV_FLAG_STREAM) || lse || p.M > kChunkRows);
+        if (use_stream) {
+            StreamParams sp;
+            memset(&sp, 0, sizeof sp);
+            sp.q = q;
+            sp.K = K;
+            sp.votes = votes;
+            sp.partial = (float2 *)(ws + p.off_st_partial);
+            sp.final_shift = (float *)(ws + p.off_st_final);
+            sp.ticket = (uint32_t *)(ws + p.off_st_ticket);
+            sp.seg_ctl = (uint32_t *)(ws + p.off_st_ctl);
+            sp.err = err;
+            sp.lse = lse;
+            sp.head_stride = p.head_stride;
+            sp.token_stride = p.token_stride;
+            sp.sum_P = p.sum_P;
+            sp.Hq = p.Hq;
+            sp.Hkv = p.Hkv;
+            sp.G = p.G;
+            sp.w = p.w;
+            sp.M = p.M;
+            sp.M_pad = p.st_rows;
+            sp.variant = p.variant;
+            sp.c = (float)(1.4426950408889634 / sqrt((double)p.d));
+            sp.slab_keys = p.st_slab;
+            sp.spin_limit = kSpinLimit;
+            sp.rt = gr.rt;
+            int64_t n = 0;
+            for (int i = 0; i < gr.rt.n; ++i) {
+                sp.rt.slab0[i] = (int32_t)n;
+                n += (int64_t)((gr.rt.L[i] + p.st_slab - 1) / p.st_slab) * p.Hkv;
+            }
+            sp.rt.slab0[gr.rt.n] = (int32_t)n;
+            int max_ns = 0;
+            (void)stream_items(p, gr, p.st_slab, &max_ns);
+            sp.n_items = (int32_t)n;
+            // Votes items trail the stats items of their segment by about one pass of the grid:
+            // close enough that part of the second read still comes from the Infinity Cache,
+            // far enough that a votes item rarely waits.
+            const int64_t lag = (int64_t)max_ns + st_grid;
+            sp.lag = (int32_t)(lag < n ? lag : n);
+            const int64_t tickets = lse ? n : 2 * n;
+            const int grid = tickets < st_grid ? (int)tickets : st_grid;
+            st = launch(SNAPKV_K_OBS_STREAM, ks, dim3(grid), dim3(st_threads), &sp, stream);
+            if (st) return st;
+            if (gr.max_P > 0 && pool) {
+                st = run_pool(p, gr, votes, pooled, stream);
+                if (st) return st;
+            }
+            continue;
+        }
         ObsParams op;
         memset(&op, 0, sizeof op);
         op.q = q;
@@ -1000,6 +1119,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_DECODE_COMBINE: return "decode_combine";
         case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
         case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
+        case SNAPKV_K_OBS_STREAM: return "obs_score_stream";
         default: return "unknown";
     }
 }

@@ -92,6 +92,34 @@ bool obs_config_short(int dtype, int d, ObsConfig *cfg);
 // Kernel entry of the chosen instantiation; keep = cached key loads.
 const void *obs_kernel(int dtype, int d, const ObsConfig &cfg, int mode, bool keep);
 
+// Streaming two-phase scoring (persistent grid, work tickets).  Items are (request, KV head,
+// slab of slab_keys keys) in request-major order; every item is visited twice: a stats pass
+// (row max and sum of exponentials over the slab's keys) and a votes pass (weights
+// normalised by the segment's merged row stats).  Ticket t maps to a pass and an item so that
+// every stats item of a segment precedes every votes item of it (lag >= items per segment).
+struct StreamParams {
+    const void *q;              // q_obs
+    const void *K;
+    float *votes;               // [H_kv][sum_P]
+    float2 *partial;            // [items][M_pad]: (shift, sum of exp2(s*c - shift)) per stats item and row
+    float *final_shift;         // [segments][M_pad]: shift + log2(sum) of the whole segment
+    uint32_t *ticket;           // one counter (own 256-byte line); returns to zero after every launch
+    uint32_t *seg_ctl;          // [segments][3 lines of 64 words]: stats done, stats ready, votes started
+    uint32_t *err;              // error word (bit 0: a wait gave up)
+    const float *lse;           // caller's row log-sum-exp [B][H_q][L_obs]: votes pass only
+    int64_t head_stride, token_stride, sum_P;
+    int32_t Hq, Hkv, G, w, M, M_pad, variant;
+    float c;                    // log2(e) / sqrt(d)
+    int32_t n_items;            // items of this group (each visited by both passes)
+    int32_t slab_keys;          // keys per item (multiple of 64)
+    int32_t lag;                // stats items issued before the first votes item
+    uint32_t spin_limit;
+    ReqTable rt;                // slab0 counts items of slab_keys
+};
+constexpr int kStreamSegLine = 64;  // uint32 words per control line
+// rows = 32, 64, 128 or 256 (>= G * L_obs), keys of 256 bytes; *threads = its workgroup size
+const void *stream_kernel(int dtype, int rows, int *threads);
+
 struct MergeParams {
     const float2 *partial;
     float2 *merged;

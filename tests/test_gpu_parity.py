@@ -31,10 +31,17 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run_and_check(wl, *, layer=0, variant=0, two_pass=False, pairs=None, token_major=False, threads=16,
-                  inputs=None):
+def stream_supported(wl):
+    """The streaming scoring kernel takes rows of 256 bytes and up to 256 query rows per KV head."""
+    row_bytes = wl.head_dim * (2 if wl.dtype == "bf16" else 4)
+    return row_bytes == 256 and wl.group * wl.obs_window <= 256
+
+
+def run_and_check(wl, *, layer=0, variant=0, two_pass=False, stream=False, pairs=None, token_major=False,
+                  threads=16, inputs=None):
     snap = _snap()
-    _say("case %s layer=%d variant=%d two_pass=%s token_major=%s" % (wl.name, layer, variant, two_pass, token_major))
+    _say("case %s layer=%d variant=%d two_pass=%s stream=%s token_major=%s" % (wl.name, layer, variant, two_pass,
+                                                                               stream, token_major))
     x = inputs if inputs is not None else synth.make_inputs(wl, layer, threads=threads)
     w, cu = wl.obs_window, x["cu_seqlens"]
     q = to_torch(x["q_obs"])
@@ -44,13 +51,14 @@ def run_and_check(wl, *, layer=0, variant=0, two_pass=False, pairs=None, token_m
         K = K.transpose(0, 1).contiguous().transpose(0, 1)
         V = V.transpose(0, 1).contiguous().transpose(0, 1)
     kw = dict(obs_window=w, pool_kernel=wl.pool_kernel, ratio=wl.ratio, budget=wl.budget)
-    spec = snap.make_spec(q, K, cu, w, wl.pool_kernel, wl.ratio, wl.budget, variant, two_pass)
+    spec = snap.make_spec(q, K, cu, w, wl.pool_kernel, wl.ratio, wl.budget, variant, two_pass, stream)
     ws = snap.workspace(spec, K.device)
-    votes, pooled = snap.scores(q, K, cu, variant=variant, two_pass=two_pass, ws=ws, **kw)
+    votes, pooled = snap.scores(q, K, cu, variant=variant, two_pass=two_pass, stream=stream, ws=ws, **kw)
     torch.cuda.synchronize()
     err_word = int(ws[:4].view(torch.int32).item())
     assert err_word == 0, "scoring reported error word %d" % err_word
-    res = snap.compress(q, K, V, cu, variant=variant, two_pass=two_pass, want_pooled=True, ws=ws, **kw)
+    res = snap.compress(q, K, V, cu, variant=variant, two_pass=two_pass, stream=stream, want_pooled=True, ws=ws,
+                        **kw)
     torch.cuda.synchronize()
     votes = votes.cpu().numpy()
     pooled_s = pooled.cpu().numpy()
@@ -114,15 +122,18 @@ def test_small_shapes(case):
                       n_plant=n_plant, name=name)
     x, _ = run_and_check(wl)
     run_and_check(wl, two_pass=True, inputs=x)
+    if stream_supported(wl):
+        run_and_check(wl, stream=True, inputs=x)
 
 
-# Fused scoring over several grid iterations of 256 workgroups: segments (KV heads) of
-# 24, 48 and 16 items (3 requests, 8 row chunks), and of 160 items (one per iteration),
-# are laid out so that none crosses an iteration boundary.
+# Fused scoring over several grid iterations of 256 workgroups (rows the streaming kernel does
+# not take: 128-byte rows, or more than 256 query rows per KV head): segments of 32, 64 and 16
+# items (3 requests, 8 row chunks of 32 rows), and of 243 items (one per iteration), are laid
+# out so that none crosses an iteration boundary.
 PACKED = [
     # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant
-    ("packed_varlen_chunks8", [5000, 11000, 3000], 32, 4, 128, "bf16", 32, 7, 0.05, None, 8),
-    ("packed_one_segment_per_iteration", [40000], 64, 2, 128, "bf16", 8, 7, 0.05, None, 8),
+    ("packed_varlen_chunks8_d64", [8000, 16000, 4000], 32, 4, 64, "bf16", 32, 7, 0.05, None, 8),
+    ("packed_one_segment_per_iteration", [40000], 64, 2, 128, "bf16", 9, 7, 0.05, None, 8),
 ]
 
 
@@ -160,8 +171,38 @@ def test_fused_packed_iterations(case):
     q, K = to_torch(x["q_obs"]), to_torch(x["K"])
     kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget)
     ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], **kw))
-    assert 1 in ids and 2 not in ids, "expected the fused scoring kernel, launched %s" % ids
+    assert 1 in ids and 2 not in ids and 15 not in ids, "expected the fused scoring kernel, launched %s" % ids
     run_and_check(wl, inputs=x)
+
+
+# The streaming two-phase kernel: grouped-query heads of 64 to 256 rows, several requests,
+# slabs of 256 to 1024 keys, more items than one pass of the grid, the prefix-only variant, a
+# request shorter than a step, and MHA forced onto it.
+STREAM = [
+    # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant, variant
+    ("stream_gqa_M256_many_items", [40000, 7000, 129], 32, 8, 128, "bf16", 64, 7, None, 2048, 16, 0),
+    ("stream_gqa_M128_varlen", [3000, 33, 16000, 9000, 700], 32, 8, 128, "bf16", 32, 7, 0.05, None, 16, 0),
+    ("stream_mha_long", [120000], 8, 8, 128, "bf16", 32, 13, 0.05, None, 64, 0),
+    ("stream_gqa_M64_f32", [5000, 12000], 4, 2, 64, "f32", 32, 7, 0.05, None, 8, 0),
+    ("stream_prefix_only_M96", [7000, 1000], 6, 2, 128, "bf16", 16, 5, 0.1, None, 8, 1),
+    ("stream_many_requests", [40 + 97 * i for i in range(40)], 8, 2, 128, "bf16", 16, 3, 0.2, None, 2, 0),
+]
+
+
+@pytest.mark.parametrize("case", STREAM, ids=[c[0] for c in STREAM])
+def test_stream_kernel(case):
+    name, lengths, Hq, Hkv, d, dt, w, kp, ratio, budget, n_plant, variant = case
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget,
+                      n_plant=n_plant, name=name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    snap = _snap()
+    q, K = to_torch(x["q_obs"]), to_torch(x["K"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, variant=variant)
+    mha = Hq == Hkv  # MHA takes the fused kernel unless the streaming one is asked for
+    ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], stream=mha, **kw))
+    assert 15 in ids and 1 not in ids, "expected the streaming scoring kernel, launched %s" % ids
+    run_and_check(wl, variant=variant, inputs=x)
+    run_and_check(wl, variant=variant, stream=True, inputs=x)
 
 
 # Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
@@ -399,6 +440,7 @@ def test_prefix_only_variant():
                       name="prefix_only")
     x, _ = run_and_check(wl, variant=1)
     run_and_check(wl, variant=1, two_pass=True, inputs=x)
+    run_and_check(wl, variant=1, stream=True, inputs=x)
 
 
 def test_token_major_layout():
