@@ -53,6 +53,7 @@ struct Dot;
 // One 16-byte operand chunk per lane = 8 bf16 = one 16x16x32 MFMA.
 template <>
 struct Dot<__bf16> {
+    static constexpr int kPerChunk = 1;  // MFMA instructions per 16-byte operand chunk
     __device__ static inline f32x4_t step(const u32x4_t &a, const u32x4_t &b, f32x4_t acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
@@ -64,6 +65,7 @@ struct Dot<__bf16> {
 // with this compiler.)
 template <>
 struct Dot<float> {
+    static constexpr int kPerChunk = 4;
     __device__ static inline f32x4_t step(const u32x4_t &a, const u32x4_t &b, f32x4_t acc) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)

@@ -71,8 +71,9 @@ __device__ inline void st_agent(uint32_t *p, uint32_t v) {
 
 }  // namespace
 
-// NW waves per workgroup (4: two workgroups per CU; 8: one), WR row waves of RTW 16-row tiles.
-template <typename T, int NW, int WR, int RTW>
+// NW waves per workgroup (4: two workgroups per CU; 8: one), WR row waves of RTW 16-row tiles,
+// DEPTH steps of keys in flight.
+template <typename T, int NW, int WR, int RTW, int DEPTH>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 obs_stream_kernel(const StreamParams p) {
     constexpr int kStreamThreads = 64 * NW;
@@ -84,7 +85,7 @@ obs_stream_kernel(const StreamParams p) {
     constexpr int MROWS = 16 * RTW * WR;  // query rows per workgroup
     static_assert(ROWB / ESZ * ESZ == ROWB, "row size");
 
-    __shared__ u32x4_t sh_k[2][NW][256];          // double-buffered step: one staged tile per wave
+    __shared__ u32x4_t sh_k[DEPTH][NW][256];      // staged steps: one tile per wave
     __shared__ float sh_v[2][NW][WR][16];         // votes of a step's tiles per row wave
     __shared__ float sh_ms[WK][MROWS], sh_ml[WK][MROWS];
     __shared__ int sh_wrow[MROWS];
@@ -111,9 +112,13 @@ obs_stream_kernel(const StreamParams p) {
     u32x4_t qf[RTW][NQ];
 
     while (ticket < total) {
-        // next ticket, fetched while this item runs
-        __syncthreads();  // everyone has read sh_ticket
-        if (tid == 0) sh_ticket = (int)__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The next ticket is drawn when this item's keys are all scored (its round trip overlaps
+        // the item's last work).  Drawing it earlier would let the first workgroups take two
+        // items each while late-starting ones find none.
+        uint32_t next_ticket = 0;
+        auto draw_next = [&]() {
+            if (tid == 0) next_ticket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
         int pass, item;
         if (lse_mode) {
             pass = 2;
@@ -150,11 +155,11 @@ obs_stream_kernel(const StreamParams p) {
             });
         }
 
-        // Row shifts of the votes pass: the segment's merged stats (or the caller's lse).
+        // Row shifts of the votes pass: the segment's merged stats (or the caller's lse).  Called
+        // once the item's first key loads are in flight, so they overlap the wait.
         float shv[RTW][4];
-        bool skip = false;
-        if (pass == 2) {
-            if (key0 >= P) skip = true;  // window keys cast no vote
+        const bool skip = pass == 2 && key0 >= P;  // window keys cast no vote
+        auto p2_prepare = [&]() {
             if (!lse_mode) {
                 // wait until the segment's stats are merged (stats items hold smaller tickets)
                 if (tid == 0) {
@@ -197,7 +202,7 @@ obs_stream_kernel(const StreamParams p) {
                     }
                 }
             }
-        }
+        };
         // prefix-only: window keys are visible to no row, so such a stats item is empty
         const bool empty_p1 = pass == 1 && p.variant != 0 && key0 >= P;
 
@@ -210,12 +215,12 @@ obs_stream_kernel(const StreamParams p) {
         float lsum[RTW][4], lsh[RTW][4];
         // mode (compile time): kP1Exp (stats pass; keys stay cached for the votes pass) or kP2
         // (votes pass; last use of the keys, non-temporal)
-        auto run_steps = [&](auto mode_c, const bool first_shift) {
+        auto run_steps = [&](auto mode_c, const bool first_shift, auto &&before_loop) {
             constexpr int mode = decltype(mode_c)::value;
             constexpr int cpol = mode == kP2 ? kNonTemporal : 0;
             static_for<RTW>([&](auto rt) { static_for<4>([&](auto i) { lsum[rt][i] = 0.f; }); });
-            // Two steps of keys in flight per wave (registers), one staged in LDS per step.
-            u32x4_t kreg[2][4];
+            // DEPTH steps of keys in flight per wave (registers), each staged in LDS when its turn comes.
+            u32x4_t kreg[DEPTH][4];
             auto load_step = [&](auto bc, int s) {
                 constexpr int B = decltype(bc)::value;
                 static_for<4>([&](auto i) {
@@ -223,23 +228,26 @@ obs_stream_kernel(const StreamParams p) {
                                                                  rsrc, lane_off, (s * kStepKeys + 4 * i) * (int)tstride, cpol));
                 });
             };
-            load_step(std::integral_constant<int, 0>{}, 0);
-            if (nsteps > 1) load_step(std::integral_constant<int, 1>{}, 1);
-            // step s (of parity B): stage its keys, start the loads of step s + 2, score
+            static_for<DEPTH>([&](auto j) {
+                if (j < nsteps) load_step(j, j);
+            });
+            before_loop();
+            // step s (slot b = s mod DEPTH): stage its keys, start the loads of step s + DEPTH, score
             auto step = [&](auto bc, const int s) {
                 constexpr int b = decltype(bc)::value;
+                const int vb = s & 1;  // votes buffer of this step
                 static_for<4>([&](auto i) {
                     const int row = 4 * i + lrow;
                     sh_k[b][wave][16 * row + (lch ^ row)] = kreg[b][i];
                 });
-                if (s + 2 < nsteps) load_step(bc, s + 2);
+                if (s + DEPTH < nsteps) load_step(bc, s + DEPTH);
                 __syncthreads();
                 if constexpr (WR > 1) {
                     // votes of the previous step, summed over the row waves
                     if (mode == kP2 && s > 0 && tid < kStepKeys) {
                         const int j = key0 + (s - 1) * kStepKeys + tid;
                         float v = 0.f;
-                        static_for<WR>([&](auto w2) { v += sh_v[b ^ 1][tid >> 4][w2][tid & 15]; });
+                        static_for<WR>([&](auto w2) { v += sh_v[vb ^ 1][tid >> 4][w2][tid & 15]; });
                         if (j < P) p.votes[(int64_t)g * p.sum_P + p.rt.pfx0[r] + j] = v;
                     }
                 }
@@ -296,23 +304,74 @@ obs_stream_kernel(const StreamParams p) {
                                 const int j = jt + n16;
                                 if (grp == 0 && (!SLOW || j < P)) p.votes[(int64_t)g * p.sum_P + p.rt.pfx0[r] + j] = v;
                             } else {
-                                if (grp == 0) sh_v[b][ti][wr][n16] = v;
+                                if (grp == 0) sh_v[vb][ti][wr][n16] = v;
                             }
                         }
                     });
                 };
-                if (s == 0 || key0 + (s + 1) * kStepKeys > P) tiles(std::true_type{});
-                else tiles(std::false_type{});
+                // The plain body, software pipelined: the LDS reads of a tile are issued one tile
+                // ahead, and the exponentials of a tile are interleaved with the MFMAs of the next,
+                // so the matrix, vector and LDS pipes work at the same time.
+                auto tiles_fast = [&]() {
+                    u32x4_t kf[2][NQ];
+                    f32x4_t S[2][RTW];
+                    auto read_tile = [&](auto slot, int ti) {
+                        const u32x4_t *stile = sh_k[b][ti];
+                        static_for<NQ>([&](auto qq) { kf[slot][qq] = stile[16 * n16 + ((4 * qq + grp) ^ n16)]; });
+                    };
+                    read_tile(std::integral_constant<int, 0>{}, wk);
+                    static_for<WR + 1>([&](auto ii) {
+                        if constexpr (ii < WR) {
+                            constexpr int cur = ii % 2;
+                            if constexpr (ii + 1 < WR) read_tile(std::integral_constant<int, (ii + 1) % 2>{}, wk + WK * (ii + 1));
+                            static_for<RTW>([&](auto rt) {
+                                S[cur][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                                static_for<NQ>([&](auto qq) { S[cur][rt] = Dot<T>::step(qf[rt][qq], kf[cur][qq], S[cur][rt]); });
+                            });
+                        }
+                        if constexpr (ii > 0) {
+                            constexpr int prev = (ii - 1) % 2;
+                            const int ti = wk + WK * (ii - 1);
+                            if constexpr (mode == kP1Exp) {
+                                static_for<RTW>([&](auto rt) {
+                                    static_for<4>([&](auto i) { lsum[rt][i] += fast_exp2(fmaf(S[prev][rt][i()], c, -lsh[rt][i])); });
+                                });
+                            } else {
+                                float v = 0.f;
+                                static_for<RTW>([&](auto rt) {
+                                    static_for<4>([&](auto i) { v += fast_exp2(fmaf(S[prev][rt][i()], c, -shv[rt][i])); });
+                                });
+                                v = cross_row_sum4(v);
+                                // every row group holds the sum: all four store it (same value, same address)
+                                if constexpr (WR == 1) {
+                                    p.votes[(int64_t)g * p.sum_P + p.rt.pfx0[r] + key0 + s * kStepKeys + ti * 16 + n16] = v;
+                                } else {
+                                    sh_v[vb][ti][wr][n16] = v;
+                                }
+                            }
+                        }
+                        if constexpr (ii > 0 && ii < WR) {
+                            // MFMAs of tile ii, one at a time between the vector work of tile ii - 1
+                            static_for<RTW * Dot<T>::kPerChunk * NQ>([&](auto) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+                            });
+                        }
+                    });
+                };
+                if ((mode == kP1Exp && first_shift && s == 0) || key0 + (s + 1) * kStepKeys > P) tiles(std::true_type{});
+                else tiles_fast();
             };
-            for (int s0 = 0; s0 < nsteps; s0 += 2) {
-                step(std::integral_constant<int, 0>{}, s0);
-                if (s0 + 1 < nsteps) step(std::integral_constant<int, 1>{}, s0 + 1);
+            for (int s0 = 0; s0 < nsteps; s0 += DEPTH) {
+                static_for<DEPTH>([&](auto j) {
+                    if (s0 + j < nsteps) step(j, s0 + j);
+                });
             }
             if constexpr (WR > 1) {
                 if (mode == kP2) {
                     __syncthreads();
                     if (tid < kStepKeys) {
-                        const int b = (nsteps - 1) & 1;
+                        const int b = (nsteps - 1) & 1;  // votes buffer of the last step
                         const int j = key0 + (nsteps - 1) * kStepKeys + tid;
                         float v = 0.f;
                         static_for<WR>([&](auto w2) { v += sh_v[b][tid >> 4][w2][tid & 15]; });
@@ -324,7 +383,9 @@ obs_stream_kernel(const StreamParams p) {
         };
 
         if (pass == 2) {
-            if (!skip) run_steps(std::integral_constant<int, kP2>{}, false);
+            if (skip) p2_prepare();
+            else run_steps(std::integral_constant<int, kP2>{}, false, p2_prepare);
+            draw_next();
         } else {
             // stats pass: per-row (shift, sum) of the slab, merged over the key groups
             auto merge_rows = [&]() {
@@ -348,7 +409,7 @@ obs_stream_kernel(const StreamParams p) {
                 // tile's shift: raise that wave-row's shift by log2 of its sum (by 64 * 2^n when
                 // the sum overflowed) and score the slab again.
                 for (int attempt = 0;; ++attempt) {
-                    run_steps(std::integral_constant<int, kP1Exp>{}, attempt == 0);
+                    run_steps(std::integral_constant<int, kP1Exp>{}, attempt == 0, [] {});
                     float lw[RTW][4];
                     static_for<RTW>([&](auto rt) { static_for<4>([&](auto i) { lw[rt][i] = row16_sum(lsum[rt][i]); }); });
                     bool bad = false;
@@ -377,6 +438,7 @@ obs_stream_kernel(const StreamParams p) {
                 }
                 merge_rows();
             }
+            draw_next();
             // the slab's (shift, sum) per row, merged over the key groups, published
             if (tid < MROWS && tid < p.M) {
                 const int row = tid;
@@ -440,8 +502,10 @@ obs_stream_kernel(const StreamParams p) {
                 }
             }
         }
+        if (tid == 0) sh_ticket = (int)next_ticket;
         __syncthreads();
         ticket = sh_ticket;
+        __syncthreads();  // everyone has read sh_ticket before it is written again
     }
     // Every workgroup draws exactly one ticket at or past the end; the last of those resets
     // the counter for the next launch.
@@ -454,10 +518,10 @@ template <typename T>
 static const void *stream_pick(int rows, int *threads) {
     *threads = rows <= 128 ? 256 : 512;
     switch (rows) {
-        case 32: return (const void *)&obs_stream_kernel<T, 4, 1, 2>;
-        case 64: return (const void *)&obs_stream_kernel<T, 4, 2, 2>;
-        case 128: return (const void *)&obs_stream_kernel<T, 4, 4, 2>;
-        default: return (const void *)&obs_stream_kernel<T, 8, 8, 2>;
+        case 32: return (const void *)&obs_stream_kernel<T, 4, 1, 2, 3>;
+        case 64: return (const void *)&obs_stream_kernel<T, 4, 2, 2, 3>;
+        case 128: return (const void *)&obs_stream_kernel<T, 4, 4, 2, 3>;
+        default: return (const void *)&obs_stream_kernel<T, 8, 8, 2, 2>;
     }
 }
 const void *stream_kernel(int dtype, int rows, int *threads) {
