@@ -38,8 +38,10 @@ sys.path.insert(0, ROOT)
 METRIC = "prompt tokens compressed/s per layer + % peak HBM GB/s (Llama-7B shape)"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD public specification
 CACHE_BYTES = 256 << 20          # MI355X Infinity Cache
-KERNEL_SOURCES = ("kv_cache_compression_amd/csrc/obs_score.hip", "kv_cache_compression_amd/csrc/obs_score_kernel.h")
-SCORING_KERNELS = ("obs_score_fused", "obs_score_stream", "obs_score_stats", "obs_stats_merge", "obs_score_votes",
+KERNEL_SOURCES = ("kv_cache_compression_amd/csrc/obs_score.hip", "kv_cache_compression_amd/csrc/obs_score_kernel.h",
+                  "kv_cache_compression_amd/csrc/obs_stream.hip", "kv_cache_compression_amd/csrc/obs_onepass.hip")
+SCORING_KERNELS = ("obs_score_onepass", "obs_score_fused", "obs_score_stream", "obs_score_stats", "obs_stats_merge",
+                   "obs_score_votes",
                    "sum_chunks")
 
 
@@ -54,6 +56,9 @@ def parse():
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="replay the timed steps as one captured HIP graph (default) or launch eagerly")
     ap.add_argument("--two-pass", action="store_true", help="force the two-pass scoring path")
+    ap.add_argument("--scoring", choices=("auto", "fused", "stream", "two-pass"), default="auto",
+                    help="scoring kernel: the library's choice (default), or force the fused, the streaming "
+                         "two-phase or the two-pass one")
     ap.add_argument("--lse", action="store_true",
                     help="time snapkv_compress_lse: each window row's log-sum-exp given (as prefill attention "
                          "would provide it), one read of K")
@@ -140,6 +145,15 @@ def profiled_traffic(workload_name):
     return float(m.group(1))
 
 
+def scoring_name(kernels_us):
+    """Which scoring path a run took, from the kernels it launched."""
+    for name, tag in (("obs_score_onepass", "one_read_stream"), ("obs_score_fused", "fused"),
+                      ("obs_score_stream", "two_phase_stream"), ("obs_score_stats", "two_pass")):
+        if name in kernels_us:
+            return tag
+    return None
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -202,7 +216,8 @@ class Run:
                 x = synth.make_inputs(wl, layer=s * self.layers_per_step + l, threads=gen_threads)
                 q, K, V = to_dev(x["q_obs"]), to_dev(x["K"]), to_dev(x["V"])
                 spec = _lib.make_spec(q, K, x["cu_seqlens"], wl.obs_window, wl.pool_kernel, wl.ratio, wl.budget,
-                                      two_pass=args.two_pass)
+                                      two_pass=args.two_pass or args.scoring == "two-pass",
+                                      stream=args.scoring == "stream", fused=args.scoring == "fused")
                 lse = row_lse(q, K, x["cu_seqlens"]) if args.lse else None
                 layers.append(dict(q=q, K=K, V=V, spec=spec, cu=x["cu_seqlens"], lse=lse,
                                    host=x if (s == 0 and l == 0) else None))
@@ -383,7 +398,8 @@ class Run:
             dom = max(scoring, key=scoring.get)
             n_l = launches.get(dom, 1.0) or 1.0
             res["dominant"] = dom
-            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_fused", "obs_score_stream",
+            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_onepass", "obs_score_fused",
+                                                                            "obs_score_stream",
                                                                             "obs_score_votes") else None
             res["dominant_launch_us"] = launch_us[dom]
         return res
@@ -571,8 +587,7 @@ def main():
                    "launch": "one graph of all timed steps" if r["launch"] == "graph" else r["launch"],
                    "kernel_timing": "traced eager steps" + (" after the graph replays" if r["launch"] == "graph"
                                                              else ""),
-                   "scoring": "lse_fed" if args.lse else ("fused" if "obs_score_fused" in r["kernels_us"]
-                                                          else "two_pass")},
+                   "scoring": "lse_fed" if args.lse else scoring_name(r["kernels_us"])},
         "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,

@@ -79,8 +79,14 @@ typedef enum { SNAPKV_CAUSAL_WINDOW = 0, SNAPKV_PREFIX_ONLY = 1 } snapkv_variant
 /* flags */
 #define SNAPKV_FLAG_TWO_PASS 0x1u /* score with two passes over K (stats, then votes) */
 #define SNAPKV_FLAG_STREAM 0x2u   /* score with the streaming two-phase kernel (rows of 256 bytes,
-                                     G * L_obs <= 256; chosen by itself for grouped-query heads,
-                                     the lse calls and problems larger than one pass of the grid) */
+                                     G * L_obs <= 256; chosen by itself for grouped-query heads
+                                     and the lse calls) */
+#define SNAPKV_FLAG_FUSED 0x4u    /* score with the fused barrier kernel (logits resident, one grid
+                                     iteration per set of whole segments).  Without a flag, rows of
+                                     256 bytes with G * L_obs <= 32 use the streaming one-read kernel
+                                     (its longest segment must fit the resident grid: 256 slabs of
+                                     2048 keys on an MI355X, i.e. 524288 tokens), then the fused
+                                     kernel, then two passes.  The three flags exclude each other. */
 
 typedef struct {
     int32_t batch;            /* B >= 1 requests */
@@ -276,7 +282,8 @@ typedef enum {
     SNAPKV_K_DECODE_COMBINE = 12, /* snapkv_decode: merge of the splits */
     SNAPKV_K_HIT_CLEAR = 13,      /* snapkv_hit_rate: zeroes the counts its tiles add to */
     SNAPKV_K_SCRATCH_CLEAR = 14,  /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
-    SNAPKV_K_OBS_STREAM = 15      /* obs_score, streaming two-phase kernel (work tickets, no barrier) */
+    SNAPKV_K_OBS_STREAM = 15,     /* obs_score, streaming two-phase kernel (work tickets, no barrier) */
+    SNAPKV_K_OBS_ONEPASS = 16     /* obs_score, streaming one-read kernel (<= 32 rows, weights resident) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

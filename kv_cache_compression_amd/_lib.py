@@ -23,6 +23,7 @@ RATIO, BUDGET = 0, 1
 CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 FLAG_STREAM = 0x2
+FLAG_FUSED = 0x4
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
            "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_compress_noalloc", "snapkv_hit_rate", "snapkv_decode_plan", "snapkv_decode",
@@ -126,7 +127,7 @@ class Spec:
 
     def __init__(self, *, batch, num_q_heads, num_kv_heads, head_dim, obs_window, pool_kernel, ratio, budget,
                  dtype, cu_seqlens, kv_head_stride, kv_token_stride, variant=CAUSAL_WINDOW, two_pass=False,
-                 stream=False):
+                 stream=False, fused=False):
         if (ratio is None) == (budget is None):
             raise ValueError("give exactly one of ratio and budget")
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
@@ -138,7 +139,7 @@ class Spec:
         pb.mode = RATIO if ratio is not None else BUDGET
         pb.dtype = dtype
         pb.variant = variant
-        pb.flags = (FLAG_TWO_PASS if two_pass else 0) | (FLAG_STREAM if stream else 0)
+        pb.flags = (FLAG_TWO_PASS if two_pass else 0) | (FLAG_STREAM if stream else 0) | (FLAG_FUSED if fused else 0)
         pb.ratio = float(ratio) if ratio is not None else 0.0
         pb.budget = int(budget) if budget is not None else 0
         pb.kv_head_stride, pb.kv_token_stride = int(kv_head_stride), int(kv_token_stride)
@@ -178,7 +179,7 @@ def _ptr(t):
 
 
 def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant=CAUSAL_WINDOW,
-              two_pass=False, stream=False) -> Spec:
+              two_pass=False, stream=False, fused=False) -> Spec:
     """Validate shapes of q_obs [B, H_q, L_obs, d] and K [H_kv, T, d] (any strides, last dim contiguous)."""
     if q_obs.dim() != 4 or K.dim() != 3:
         raise ValueError("q_obs must be [B, H_q, L_obs, d] and K [H_kv, T, d]")
@@ -200,7 +201,7 @@ def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, vari
     return Spec(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, obs_window=obs_window,
                 pool_kernel=pool_kernel, ratio=ratio, budget=budget, dtype=_dtype_code(K), cu_seqlens=cu,
                 kv_head_stride=K.stride(0), kv_token_stride=K.stride(1), variant=variant, two_pass=two_pass,
-                stream=stream)
+                stream=stream, fused=fused)
 
 
 def workspace(spec: Spec, device) -> torch.Tensor:
@@ -242,15 +243,16 @@ def _check_lse(lse, q_obs):
 
 def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
            variant=CAUSAL_WINDOW, two_pass=False, want_votes=True, ws=None, lse=None, check_errors=True,
-           stream=False):
+           stream=False, fused=False):
     """snapkv_scores (snapkv_scores_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs] is
-    given): returns (votes or None, pooled), float32 [H_kv, sum_P].  two_pass / stream force the
-    two-pass or the streaming scoring kernel (SNAPKV_FLAG_TWO_PASS / SNAPKV_FLAG_STREAM).
+    given): returns (votes or None, pooled), float32 [H_kv, sum_P].  two_pass / stream / fused
+    force the two-pass, the streaming two-phase or the fused scoring kernel (SNAPKV_FLAG_TWO_PASS /
+    SNAPKV_FLAG_STREAM / SNAPKV_FLAG_FUSED); by default the library chooses.
 
     check_errors: wait for the stream and raise SnapKVError if the workspace's error word
     is set (see error_word_view).  With check_errors=False nothing waits; read the word
     later with read_error_word(ws) (pass your own ws to do so)."""
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream)
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused)
     dev = K.device
     votes = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev) if want_votes else None
     pooled = torch.empty((spec.Hkv, spec.sum_P), dtype=torch.float32, device=dev)
@@ -302,7 +304,7 @@ def gather(K, V, idx, q_obs, cu_seqlens=None, *, obs_window=32, pool_kernel=7, r
 
 def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
              variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None, lse=None,
-             check_errors=True, stream=False):
+             check_errors=True, stream=False, fused=False):
     """snapkv_compress (snapkv_compress_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs]
     is given): the whole path.
 
@@ -315,7 +317,7 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
     (a scoring barrier gave up, or the workspace was not clean).  check_errors=False returns at
     once; read res["error_word"] after the stream has reached the call.
     """
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream)
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused)
     if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
         raise ValueError("V must match K in shape, strides and dtype")
     dev = K.device
@@ -351,12 +353,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # SNAPKV_NOALLOC_SCRATCH_BYTES
 
 
 def compress_noalloc(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-                     variant=CAUSAL_WINDOW, two_pass=False, out=None, error_word=None):
+                     variant=CAUSAL_WINDOW, two_pass=False, out=None, error_word=None, stream=False, fused=False):
     """snapkv_compress_noalloc: the whole path with the library's own device scratch as the
     workspace (the C call allocates nothing; the outputs are allocated here unless `out` gives
     them).  error_word: optional int32 device tensor of one element that receives the call's
     error bits.  Returns the same dict as compress() (without pooled unless out holds it)."""
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass)
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused)
     if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
         raise ValueError("V must match K in shape, strides and dtype")
     dev = K.device

@@ -60,7 +60,8 @@ struct Plan {
     // workspace layout (bytes)
     size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx;
     size_t off_long_state, off_ghist, off_cand, off_tilecnt;
-    size_t off_st_ticket, off_st_ctl, off_st_partial, off_st_final, ws_bytes;
+    size_t off_st_ticket, off_st_ctl, off_st_partial, off_st_final;
+    size_t off_op_partial, off_op_final, ws_bytes;  // one-read kernel: tagged row stats, row shifts
 };
 
 // Streaming scoring: grid of two workgroups per CU (the plan assumes the MI355X's 256 CUs;
@@ -163,9 +164,13 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.dtype != SNAPKV_F32 && p.dtype != SNAPKV_BF16) return fail(SNAPKV_EINVAL, "dtype must be F32 or BF16");
     if (p.variant != SNAPKV_CAUSAL_WINDOW && p.variant != SNAPKV_PREFIX_ONLY)
         return fail(SNAPKV_EINVAL, "variant must be CAUSAL_WINDOW or PREFIX_ONLY");
-    if (p.flags & ~(SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM)) return fail(SNAPKV_EINVAL, "unknown flag bits");
-    if ((p.flags & SNAPKV_FLAG_TWO_PASS) && (p.flags & SNAPKV_FLAG_STREAM))
-        return fail(SNAPKV_EINVAL, "SNAPKV_FLAG_TWO_PASS and SNAPKV_FLAG_STREAM exclude each other");
+    if (p.flags & ~(SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED))
+        return fail(SNAPKV_EINVAL, "unknown flag bits");
+    {
+        const uint32_t path = p.flags & (SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED);
+        if (path & (path - 1))
+            return fail(SNAPKV_EINVAL, "SNAPKV_FLAG_TWO_PASS, SNAPKV_FLAG_STREAM and SNAPKV_FLAG_FUSED exclude each other");
+    }
     if (p.mode == SNAPKV_RATIO && !(p.ratio > 0.0 && p.ratio <= 1.0))
         return fail(SNAPKV_EINVAL, "ratio must lie in (0, 1]");
     if (p.mode == SNAPKV_BUDGET && p.budget < 0) return fail(SNAPKV_EINVAL, "budget must be >= 0");
@@ -305,6 +310,13 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.st_ok) off = align_up(off + sizeof(float) * 2 * st_rows * (size_t)p.st_max_items);
     p.off_st_final = off;
     if (p.st_ok) off = align_up(off + sizeof(float) * st_rows * (size_t)p.max_group_segs);
+    // one-read scoring (32 rows): per-item row stats and per-segment row shifts, both tagged so
+    // that zero means "not yet written"; every call leaves them at zero
+    const bool op_ok = p.st_ok && p.st_rows == 32;
+    p.off_op_partial = off;
+    if (op_ok) off = align_up(off + sizeof(float) * 2 * 32 * (size_t)p.st_max_items);
+    p.off_op_final = off;
+    if (op_ok) off = align_up(off + sizeof(float) * 32 * (size_t)p.max_group_segs);
     p.ws_bytes = off;
     return SNAPKV_OK;
 }
@@ -439,22 +451,34 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
     int st_threads = 0;
     const void *ks = p.st_ok ? stream_kernel(p.dtype, p.st_rows, &st_threads) : nullptr;
     const int st_grid = p.st_ok ? occupancy(ks, st_threads) * di.cus : 0;
+    int op_threads = 0, op_slab = 0;
+    const void *ko = p.st_ok && p.st_rows == 32 ? onepass_kernel(p.dtype, &op_threads, &op_slab) : nullptr;
+    const int op_grid = ko ? occupancy(ko, op_threads) * di.cus : 0;
+    const bool forced = (p.flags & (SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED)) != 0;
     for (const Group &gr : p.groups) {
-        // The streaming kernel takes grouped-query heads, the caller's row stats, and problems
-        // whose logits do not fit one pass of the resident grid; the fused kernel the rest.
-        const int64_t fused_items = (int64_t)gr.n_slabs * C;
-        // Grouped-query heads and the caller's row stats go to the streaming kernel (it reads each
-        // key once for all of a group's rows); MHA stays with the fused kernel, which reads K once.
-        (void)fused_items;
-        const bool use_stream = p.st_ok && st_grid > 0 && ((p.flags & SNAPKV_FLAG_STREAM) || lse || p.M > kChunkRows);
-        if (use_stream) {
+        int max_ns = 0;
+        if (p.st_ok) (void)stream_items(p, gr, p.st_slab, &max_ns);
+        int op_max_ns = 0;
+        const int64_t op_items = ko ? stream_items(p, gr, op_slab, &op_max_ns) : 0;
+        // Up to 32 rows per KV head: the one-read streaming kernel when all of the group's items
+        // fit one pass of the resident grid (its segment waits then cost one tail, and they
+        // need the segment's items resident at once); past that its waits grow with the
+        // segment's share of the grid, and the two-phase streaming kernel, which reads K twice
+        // (the second time partly from the Infinity Cache) but never waits on a slower item,
+        // is faster (825 against 965 us at the 380K-token layer).  Grouped-query heads and the
+        // caller's row stats: the two-phase kernel too (it reads each key once per pass for all
+        // of a group's rows).  Otherwise the fused kernel, else two passes.
+        const bool use_onepass = ko && !lse && !forced && op_grid > 0 && op_items <= op_grid && op_max_ns <= op_grid;
+        const bool use_stream = !use_onepass && p.st_ok && st_grid > 0 && !(p.flags & SNAPKV_FLAG_FUSED) &&
+                                !(p.flags & SNAPKV_FLAG_TWO_PASS);
+        if (use_onepass || use_stream) {
             StreamParams sp;
             memset(&sp, 0, sizeof sp);
             sp.q = q;
             sp.K = K;
             sp.votes = votes;
-            sp.partial = (float2 *)(ws + p.off_st_partial);
-            sp.final_shift = (float *)(ws + p.off_st_final);
+            sp.partial = (float2 *)(ws + (use_onepass ? p.off_op_partial : p.off_st_partial));
+            sp.final_shift = (float *)(ws + (use_onepass ? p.off_op_final : p.off_st_final));
             sp.ticket = (uint32_t *)(ws + p.off_st_ticket);
             sp.seg_ctl = (uint32_t *)(ws + p.off_st_ctl);
             sp.err = err;
@@ -470,26 +494,32 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
             sp.M_pad = p.st_rows;
             sp.variant = p.variant;
             sp.c = (float)(1.4426950408889634 / sqrt((double)p.d));
-            sp.slab_keys = p.st_slab;
+            // the one-read kernel always takes its largest slab: it runs every step of an item
+            // whatever the slab's length
+            const int slab_keys = use_onepass ? op_slab : p.st_slab;
+            sp.slab_keys = slab_keys;
             sp.spin_limit = kSpinLimit;
             sp.rt = gr.rt;
             int64_t n = 0;
             for (int i = 0; i < gr.rt.n; ++i) {
                 sp.rt.slab0[i] = (int32_t)n;
-                n += (int64_t)((gr.rt.L[i] + p.st_slab - 1) / p.st_slab) * p.Hkv;
+                n += (int64_t)((gr.rt.L[i] + slab_keys - 1) / slab_keys) * p.Hkv;
             }
             sp.rt.slab0[gr.rt.n] = (int32_t)n;
-            int max_ns = 0;
-            (void)stream_items(p, gr, p.st_slab, &max_ns);
             sp.n_items = (int32_t)n;
-            // Votes items trail the stats items of their segment by about one pass of the grid:
-            // close enough that part of the second read still comes from the Infinity Cache,
-            // far enough that a votes item rarely waits.
-            const int64_t lag = (int64_t)max_ns + st_grid;
-            sp.lag = (int32_t)(lag < n ? lag : n);
-            const int64_t tickets = lse ? n : 2 * n;
-            const int grid = tickets < st_grid ? (int)tickets : st_grid;
-            st = launch(SNAPKV_K_OBS_STREAM, ks, dim3(grid), dim3(st_threads), &sp, stream);
+            if (use_onepass) {
+                const int grid = n < op_grid ? (int)n : op_grid;
+                st = launch(SNAPKV_K_OBS_ONEPASS, ko, dim3(grid), dim3(op_threads), &sp, stream);
+            } else {
+                // Votes items trail the stats items of their segment by about one pass of the grid:
+                // close enough that part of the second read still comes from the Infinity Cache,
+                // far enough that a votes item rarely waits.
+                const int64_t lag = (int64_t)max_ns + st_grid;
+                sp.lag = (int32_t)(lag < n ? lag : n);
+                const int64_t tickets = lse ? n : 2 * n;
+                const int grid = tickets < st_grid ? (int)tickets : st_grid;
+                st = launch(SNAPKV_K_OBS_STREAM, ks, dim3(grid), dim3(st_threads), &sp, stream);
+            }
             if (st) return st;
             if (gr.max_P > 0 && pool) {
                 st = run_pool(p, gr, votes, pooled, stream);
@@ -1120,6 +1150,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
         case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
         case SNAPKV_K_OBS_STREAM: return "obs_score_stream";
+        case SNAPKV_K_OBS_ONEPASS: return "obs_score_onepass";
         default: return "unknown";
     }
 }

@@ -167,6 +167,13 @@ __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
 }
+// The same for a wave-uniform value (kept in an SGPR): a per-tile load offset formed from it is
+// computed where the load is issued, instead of every tile's offset being precomputed and held
+// in VGPRs across the whole unrolled slab.
+__device__ __forceinline__ int opaque_s(int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
 
 // Key loads: non-temporal when every key is read once, cached when the row chunks of a
 // slab read it again.
@@ -289,9 +296,11 @@ __global__ void __launch_bounds__(64 * WR * WK) obs_score_kernel(const ObsParams
             u32x4_t buf[PF][4];
             auto load_tile = [&](auto slot, int ct) {
                 static_for<4>([&](auto i) {
-                    const int soff = (ct * WK * 16 + 4 * i) * (int)tstride;  // wave-uniform
+                    // the whole offset in the VGPR operand (soffset 0), which the buffer range
+                    // check covers: tiles past the slab's keys read zeros
+                    const int soff = opaque_s((ct * WK * 16 + 4 * i) * (int)tstride);  // wave-uniform
                     buf[slot][i] = __builtin_bit_cast(
-                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off, soff, KEEP ? 0 : kNonTemporal));
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + soff, 0, KEEP ? 0 : kNonTemporal));
                 });
             };
             static_for<(PF < CTW ? PF : CTW)>([&](auto f) { load_tile(f, f); });

@@ -224,8 +224,10 @@ obs_stream_kernel(const StreamParams p) {
             auto load_step = [&](auto bc, int s) {
                 constexpr int B = decltype(bc)::value;
                 static_for<4>([&](auto i) {
+                    // whole offset in the VGPR operand (soffset 0): the range check covers it
                     kreg[B][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                 rsrc, lane_off, (s * kStepKeys + 4 * i) * (int)tstride, cpol));
+                                                                 rsrc, lane_off + opaque_s((s * kStepKeys + 4 * i) * (int)tstride),
+                                                                 0, cpol));
                 });
             };
             static_for<DEPTH>([&](auto j) {

@@ -112,13 +112,16 @@ struct StreamParams {
     float c;                    // log2(e) / sqrt(d)
     int32_t n_items;            // items of this group (each visited by both passes)
     int32_t slab_keys;          // keys per item (multiple of 64)
-    int32_t lag;                // stats items issued before the first votes item
+    int32_t lag;                // stats items issued before the first votes item (two-phase kernel)
     uint32_t spin_limit;
     ReqTable rt;                // slab0 counts items of slab_keys
 };
 constexpr int kStreamSegLine = 64;  // uint32 words per control line
 // rows = 32, 64, 128 or 256 (>= G * L_obs), keys of 256 bytes; *threads = its workgroup size
 const void *stream_kernel(int dtype, int rows, int *threads);
+// one-read streaming kernel for up to 32 rows per KV head, keys of 256 bytes; *threads = its
+// workgroup size, *slab = the keys of one item
+const void *onepass_kernel(int dtype, int *threads, int *slab);
 
 struct MergeParams {
     const float2 *partial;

@@ -37,11 +37,11 @@ def stream_supported(wl):
     return row_bytes == 256 and wl.group * wl.obs_window <= 256
 
 
-def run_and_check(wl, *, layer=0, variant=0, two_pass=False, stream=False, pairs=None, token_major=False,
-                  threads=16, inputs=None):
+def run_and_check(wl, *, layer=0, variant=0, two_pass=False, stream=False, fused=False, pairs=None,
+                  token_major=False, threads=16, inputs=None):
     snap = _snap()
-    _say("case %s layer=%d variant=%d two_pass=%s stream=%s token_major=%s" % (wl.name, layer, variant, two_pass,
-                                                                               stream, token_major))
+    _say("case %s layer=%d variant=%d two_pass=%s stream=%s fused=%s token_major=%s" % (
+        wl.name, layer, variant, two_pass, stream, fused, token_major))
     x = inputs if inputs is not None else synth.make_inputs(wl, layer, threads=threads)
     w, cu = wl.obs_window, x["cu_seqlens"]
     q = to_torch(x["q_obs"])
@@ -51,14 +51,15 @@ def run_and_check(wl, *, layer=0, variant=0, two_pass=False, stream=False, pairs
         K = K.transpose(0, 1).contiguous().transpose(0, 1)
         V = V.transpose(0, 1).contiguous().transpose(0, 1)
     kw = dict(obs_window=w, pool_kernel=wl.pool_kernel, ratio=wl.ratio, budget=wl.budget)
-    spec = snap.make_spec(q, K, cu, w, wl.pool_kernel, wl.ratio, wl.budget, variant, two_pass, stream)
+    spec = snap.make_spec(q, K, cu, w, wl.pool_kernel, wl.ratio, wl.budget, variant, two_pass, stream, fused)
     ws = snap.workspace(spec, K.device)
-    votes, pooled = snap.scores(q, K, cu, variant=variant, two_pass=two_pass, stream=stream, ws=ws, **kw)
+    votes, pooled = snap.scores(q, K, cu, variant=variant, two_pass=two_pass, stream=stream, fused=fused, ws=ws,
+                                **kw)
     torch.cuda.synchronize()
     err_word = int(ws[:4].view(torch.int32).item())
     assert err_word == 0, "scoring reported error word %d" % err_word
-    res = snap.compress(q, K, V, cu, variant=variant, two_pass=two_pass, stream=stream, want_pooled=True, ws=ws,
-                        **kw)
+    res = snap.compress(q, K, V, cu, variant=variant, two_pass=two_pass, stream=stream, fused=fused,
+                        want_pooled=True, ws=ws, **kw)
     torch.cuda.synchronize()
     votes = votes.cpu().numpy()
     pooled_s = pooled.cpu().numpy()
@@ -124,6 +125,8 @@ def test_small_shapes(case):
     run_and_check(wl, two_pass=True, inputs=x)
     if stream_supported(wl):
         run_and_check(wl, stream=True, inputs=x)
+        if wl.group * wl.obs_window <= 32:  # the default there is the one-read kernel
+            run_and_check(wl, fused=True, inputs=x)
 
 
 # Fused scoring over several grid iterations of 256 workgroups (rows the streaming kernel does
@@ -198,11 +201,45 @@ def test_stream_kernel(case):
     snap = _snap()
     q, K = to_torch(x["q_obs"]), to_torch(x["K"])
     kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, variant=variant)
-    mha = Hq == Hkv  # MHA takes the fused kernel unless the streaming one is asked for
+    mha = Hq == Hkv  # MHA takes the one-read kernel unless the two-phase one is asked for
     ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], stream=mha, **kw))
     assert 15 in ids and 1 not in ids, "expected the streaming scoring kernel, launched %s" % ids
     run_and_check(wl, variant=variant, inputs=x)
     run_and_check(wl, variant=variant, stream=True, inputs=x)
+
+
+# The one-read streaming kernel (the default for up to 32 rows of 256 bytes per KV head when a
+# layer's 2048-key items fit one pass of the 256 resident workgroups):
+# segments that merge per item (at most 32 items) and through the published shifts (more:
+# 40000 tokens are 20 items, 70000 are 35),
+# ragged slab tails, a request shorter than one step, a request with an empty prefix, grouped
+# heads of 15 and 32 rows, fp32, the prefix-only variant, and a segment of 245 items (near the
+# 256 workgroups the MI355X keeps resident).
+ONEPASS = [
+    # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant, variant
+    ("onepass_mha_ragged", [5000, 1024, 2100, 40], 8, 8, 128, "bf16", 32, 7, 0.05, None, 16, 0),
+    ("onepass_central_merge", [70000, 66000, 900], 2, 2, 128, "bf16", 32, 13, 0.05, None, 32, 0),
+    ("onepass_empty_prefix", [32, 3000, 64], 4, 4, 128, "bf16", 32, 7, 0.1, None, 4, 0),
+    ("onepass_gqa_M15", [4000, 900], 6, 2, 128, "bf16", 5, 3, 0.1, None, 8, 0),
+    ("onepass_gqa_M32_f32_d64", [6000], 4, 2, 64, "f32", 16, 7, None, 200, 8, 0),
+    ("onepass_prefix_only", [9000, 1500], 4, 4, 128, "bf16", 32, 7, 0.05, None, 8, 1),
+    ("onepass_245_items", [500000], 1, 1, 128, "bf16", 32, 7, 0.05, None, 64, 0),
+]
+
+
+@pytest.mark.parametrize("case", ONEPASS, ids=[c[0] for c in ONEPASS])
+def test_onepass_kernel(case):
+    name, lengths, Hq, Hkv, d, dt, w, kp, ratio, budget, n_plant, variant = case
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget,
+                      n_plant=n_plant, name=name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    snap = _snap()
+    q, K = to_torch(x["q_obs"]), to_torch(x["K"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, variant=variant)
+    ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], **kw))
+    assert 16 in ids and 1 not in ids and 15 not in ids, "expected the one-read scoring kernel, launched %s" % ids
+    run_and_check(wl, variant=variant, inputs=x)
+    run_and_check(wl, variant=variant, token_major=True, inputs=x)
 
 
 # Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
