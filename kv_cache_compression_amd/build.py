@@ -35,9 +35,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsnapkv)")
 
 
-def _compile(src: str, obj: str) -> str:
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                     os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizers for the plan and validation code in api.hip (a test build; each flag goes
+# to the host pass only, the device code is built as usual).
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src: str, obj: str, extra=()) -> str:
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-c", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+                                                   os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln)
@@ -46,19 +52,23 @@ def _compile(src: str, obj: str) -> str:
     return err
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
+def build(verbose: bool = False, jobs: int = 0, out: str | None = None, host_sanitize: bool = False) -> str:
     """Compile every HIP source into kv_cache_compression_amd/libsnapkv.so (always rebuilds).
-    The sources compile in parallel (one hipcc per source), then link into one library."""
+    The sources compile in parallel (one hipcc per source), then link into one library.
+    out / host_sanitize: a test build elsewhere whose api.hip host code carries AddressSanitizer and
+    UndefinedBehaviorSanitizer checks (load it with the sanitizer runtime preloaded)."""
     from concurrent.futures import ThreadPoolExecutor
-    tag = "%d" % os.getpid()
+    lib = out or LIB
+    tag = "%d%s" % (os.getpid(), "s" if host_sanitize else "")
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.splitext(s)[0] + "." + tag + ".o") for s in SOURCES]
+    extras = [HOST_SANITIZE_FLAGS if (host_sanitize and s == "api.hip") else [] for s in SOURCES]
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     try:
         with ThreadPoolExecutor(max_workers=jobs) as ex:
-            msgs = list(ex.map(_compile, SOURCES, objs))
-        tmp = LIB + ".tmp" + tag
+            msgs = list(ex.map(_compile, SOURCES, objs, extras))
+        tmp = lib + ".tmp" + tag
         res = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
                              capture_output=True, text=True)
         if res.returncode != 0:
@@ -71,8 +81,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         for m in msgs:
             if m.strip():
                 print(m, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -63,7 +63,9 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            lib = ctypes.CDLL(build())
+            # SNAPKV_ORACLE_LIB: a separately built copy of the same source (the sanitizer test
+            # builds one with AddressSanitizer and UndefinedBehaviorSanitizer)
+            lib = ctypes.CDLL(os.environ.get("SNAPKV_ORACLE_LIB") or build())
             vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
             lib.snapkv_oracle_votes.argtypes = [vp, ctypes.c_int, i64, i32, i32, vp, i64, i64, i32, vp, vp]
             lib.snapkv_oracle_votes.restype = None
