@@ -104,9 +104,16 @@ obs_stream_kernel(const StreamParams p) {
     const int64_t tstride = p.token_stride * ESZ;
 
     for (int r = tid; r < MROWS; r += kStreamThreads) sh_wrow[r] = r % p.w;  // rows of a chunk start at 0
-    if (tid == 0) sh_ticket = (int)__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // With the caller's row stats no item waits for another, so a workgroup's first ticket is its
+    // own index (a grid of 512 drawing from one counter at launch spreads the starts over ~6 us)
+    // and the counter hands out gridDim.x + n.  With the stats pass, votes items wait for stats
+    // items with smaller tickets, and every ticket comes from the counter, so that a drawn ticket
+    // is always held by a running workgroup.
+    const int t_base = lse_mode ? (int)gridDim.x : 0;
+    if (tid == 0 && !lse_mode)
+        sh_ticket = (int)__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    int ticket = sh_ticket;
+    int ticket = lse_mode ? (int)blockIdx.x : sh_ticket;
 
     int cur_seg = -1;
     u32x4_t qf[RTW][NQ];
@@ -504,13 +511,13 @@ obs_stream_kernel(const StreamParams p) {
                 }
             }
         }
-        if (tid == 0) sh_ticket = (int)next_ticket;
+        if (tid == 0) sh_ticket = t_base + (int)next_ticket;
         __syncthreads();
         ticket = sh_ticket;
         __syncthreads();  // everyone has read sh_ticket before it is written again
     }
     // Every workgroup draws exactly one ticket at or past the end; the last of those resets
-    // the counter for the next launch.
+    // the counter for the next launch (the counter's last value is total + gridDim.x - 1 - t_base).
     if (tid == 0 && ticket == total + (int)gridDim.x - 1) st_agent(p.ticket, 0u);
 }
 
