@@ -118,14 +118,21 @@ typedef struct {
  *                       snapkv_compress need for this problem (device
  *                       independent; 0 is never returned).
  * Workspace contract: zero-fill it once before its first use.  Every call
- * leaves its barrier counters at zero again, so later calls (also under graph
- * replay) need no clearing.  The first 4 bytes hold a sticky error word that
- * only the caller clears: bit 0 = a per-segment barrier gave up waiting (only
- * possible if other work kept part of the scoring grid off the GPU for about a
- * second); bit 1 = a barrier counter was not zero when a call started (the
- * workspace was not zero-filled, or was shared by calls running at the same
- * time).  With either bit set the outputs of the calls since it was last clear
- * may be invalid; SNAPKV_FLAG_TWO_PASS, which has no barrier, computes them.
+ * leaves its counters and tagged slots at zero again, so later calls (also
+ * under graph replay) need no clearing.  The first 4 bytes hold a sticky error
+ * word that only the caller clears:
+ *   bit 0 = a scoring workgroup gave up waiting for others of its launch.  The
+ *           fused and the one-read kernels need all workgroups of a (request,
+ *           KV head) segment resident at once (their grid never exceeds what the
+ *           device keeps resident); other work holding part of the GPU for
+ *           about a second can break that.  The two-phase streaming kernel only
+ *           waits for workgroups already running.
+ *   bit 1 = a counter was not zero when a call started (the workspace was not
+ *           zero-filled, or was shared by calls running at the same time).
+ *   bit 2 = a row's sum of exponentials still overflowed after 8 raises of its
+ *           shift (needs logits spanning more than about 2^100 in one slab).
+ * With any bit set the outputs of the calls since it was last clear may be
+ * invalid; SNAPKV_FLAG_TWO_PASS, which has no wait and no shift, computes them.
  * Returns SNAPKV_OK or SNAPKV_EINVAL / SNAPKV_EUNSUPPORTED.
  */
 int snapkv_plan(const snapkv_problem *pb, int64_t *k_host, int64_t *cu_pfx_host, int64_t *cu_k_host,

@@ -213,11 +213,12 @@ def workspace(spec: Spec, device) -> torch.Tensor:
 
 def error_word_view(ws: torch.Tensor) -> torch.Tensor:
     """The workspace's sticky error word as a 1-element int32 device view (valid once the
-    stream has reached the calls that wrote it).  Bit 0: a scoring barrier gave up waiting
-    (another kernel kept part of the scoring grid off the device); bit 1: a barrier counter
-    was not zero when a call started (the workspace was not zero-filled, or was shared by
-    calls running at the same time).  Either bit means the outputs since it was last clear
-    may be wrong; the library never clears it."""
+    stream has reached the calls that wrote it).  Bit 0: a scoring workgroup gave up waiting
+    for others of its launch (another kernel kept part of the scoring grid off the device);
+    bit 1: a counter was not zero when a call started (the workspace was not zero-filled, or
+    was shared by calls running at the same time); bit 2: a row's sum of exponentials still
+    overflowed after 8 raises of its shift.  Any bit means the outputs since it was last
+    clear may be wrong; the library never clears it."""
     return ws[:4].view(torch.int32)
 
 
