@@ -17,9 +17,10 @@
 //     (never for ordinary inputs; past 8 raises error bit 2 is set).
 //   * The items of a segment then meet, through per-item row stats that carry a validity tag
 //     (zero means "not written yet"), so no arrival count sits on the path.  Short segments (at
-//     most kSelfMerge items): each item publishes its (shift, sum) per row and polls every item's
-//     slot of its rows until all are written, then merges them itself; a count of readers, taken
-//     off the path, lets the last reader clear the slots.  Longer segments: an arrival count finds
+//     most kSelfMerge items): each item publishes its (shift, sum) per row; one wave of each item
+//     polls every item's slots until all are written (one wave keeps the poll traffic beside the
+//     still-running key streams small), merges them and hands the shifts to the other waves; a
+//     count of readers, taken off the path, lets the last reader clear the slots.  Longer segments: an arrival count finds
 //     the last item, which merges once and publishes tagged row shifts that the others poll; the
 //     last reader clears them.  Every slot and count is back at zero when the launch ends.
 //   * Each item then scales its resident weights by exp2(shift_wave - shift_segment), where the
@@ -65,6 +66,7 @@ obs_onepass_kernel(const StreamParams p) {
     constexpr int MROWS = 16 * RTW;
     constexpr int TPR = NT / MROWS;  // threads per row in the stats merge
     static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0, "threads per row");
+    static_assert(MROWS == 32, "a wave polls two items per row per load round");
 
     __shared__ u32x4_t sh_k[NW][256];  // each wave's staging tile (no other wave touches it)
     __shared__ float sh_ms[NW][MROWS], sh_ml[NW][MROWS];
@@ -265,52 +267,61 @@ obs_onepass_kernel(const StreamParams p) {
         uint32_t *const done_ctr = p.seg_ctl + (int64_t)seg * 3 * kStreamSegLine;
         uint32_t *const readers = done_ctr + 2 * kStreamSegLine;
         uint32_t *const fin_slot = (uint32_t *)p.final_shift + (int64_t)seg * MROWS;  // ~bits of the shift, 0 = unwritten
-        const int row_m = tid / TPR, sub = tid - (tid / TPR) * TPR;
-        // merge of (shift, sum) slots of this thread's row: items sub, sub + TPR, ...
-        float mm = neg_inf(), ll = 0.f;
-        auto merge_word = [&](uint64_t wd) {
+        auto merge_word = [](float &mm, float &ll, uint64_t wd) {
             merge_stats(mm, ll, __uint_as_float((uint32_t)wd), __uint_as_float((uint32_t)(wd >> 32) & ~kTag), 1.f);
         };
-        auto finish_row = [&]() {
-#pragma unroll
-            for (int o = 1; o < TPR; o <<= 1) {
-                const float m2 = __shfl_xor(mm, o, TPR);
-                const float l2 = __shfl_xor(ll, o, TPR);
-                merge_stats(mm, ll, m2, l2, 1.f);
-            }
-            return row_m < p.M && ll > 0.f ? mm + __builtin_amdgcn_logf(ll) : __builtin_huge_valf();
-        };
-        bool last_item = false;
+        uint32_t next = 0;         // the next item's draw (thread 0)
+        bool last_item = false;    // long segments: this item merged for the segment
+        uint32_t read_before = 0;  // readers of the slots (short) or shifts (long) before this item
         if (self_merge) {
-            // poll this thread's slots (at most kSelfMerge / TPR) until every one is written
-            constexpr int kPer = (kSelfMerge + TPR - 1) / TPR;
-            if (row_m < p.M) {
-                uint64_t wd[kPer];
-                uint32_t spins = 0;
-                for (;;) {
-                    bool all = true;
-                    static_for<kPer>([&](auto b) {
-                        const int it = sub + b() * TPR;
-                        wd[b()] = it < ns ? __hip_atomic_load(&slots[(int64_t)(item0 + it) * MROWS + row_m],
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                          : ~0ull;
-                        all = all && wd[b()] != 0ull;
-                    });
-                    if (all) break;
-                    __builtin_amdgcn_s_sleep(2);
-                    if (++spins > p.spin_limit) {
-                        __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
+            // Wave 0 polls all of the segment's slots (row lane % 32, items lane / 32, +2, ...;
+            // eight items per round of loads) until each is written, merges them and hands the
+            // shifts to the other waves through LDS.  One polling wave per workgroup keeps the
+            // poll traffic, which shares the memory system with the key streams still running,
+            // small.
+            if (wave == 0) {
+                constexpr int kPerLane = 4;
+                const int row_l = lane & (MROWS - 1), half = lane >> 5;
+                float mm = neg_inf(), ll = 0.f;
+                if (row_l < p.M) {
+                    for (int it0 = half; it0 < ns; it0 += 2 * kPerLane) {
+                        uint64_t wd[kPerLane];
+                        uint32_t spins = 0;
+                        for (;;) {
+                            bool all = true;
+                            static_for<kPerLane>([&](auto b) {
+                                const int it = it0 + 2 * b();
+                                wd[b()] = it < ns ? __hip_atomic_load(&slots[(int64_t)(item0 + it) * MROWS + row_l],
+                                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                                  : ~0ull;
+                                all = all && wd[b()] != 0ull;
+                            });
+                            if (all) break;
+                            __builtin_amdgcn_s_sleep(8);
+                            if (++spins > p.spin_limit) {
+                                __hip_atomic_fetch_or(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                break;
+                            }
+                        }
+                        static_for<kPerLane>([&](auto b) {
+                            if (it0 + 2 * b() < ns) merge_word(mm, ll, wd[b()]);
+                        });
                     }
                 }
-                static_for<kPer>([&](auto b) {
-                    if (sub + b() * TPR < ns) merge_word(wd[b()]);
-                });
+                merge_stats(mm, ll, __shfl_xor(mm, 32), __shfl_xor(ll, 32), 1.f);
+                if (half == 0) sh_fin[row_l] = row_l < p.M && ll > 0.f ? mm + __builtin_amdgcn_logf(ll) : __builtin_huge_valf();
             }
-            const float fin = finish_row();
-            if (sub == 0) sh_fin[row_m] = fin;
+            __syncthreads();
+            // The segment is complete: draw the next item and count this item's read of the slots.
+            // Issued after the barrier (whose release fence would wait for them), so both round
+            // trips overlap the votes.
+            if (tid == 0) {
+                next = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                read_before = __hip_atomic_fetch_add(readers, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         } else {
             // the last arrival merges once and publishes the shifts
+            const int row_m = tid / TPR, sub = tid - (tid / TPR) * TPR;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (tid == 0) {
@@ -321,6 +332,7 @@ obs_onepass_kernel(const StreamParams p) {
             __syncthreads();
             last_item = sh_flag != 0;
             if (last_item) {
+                float mm = neg_inf(), ll = 0.f;
                 if (row_m < p.M) {
                     for (int s0 = sub; s0 < ns; s0 += 8 * TPR) {
                         uint64_t bits[8];
@@ -330,11 +342,17 @@ obs_onepass_kernel(const StreamParams p) {
                                                            __HIP_MEMORY_SCOPE_AGENT);
                         });
                         static_for<8>([&](auto bb) {
-                            if (s0 + bb() * TPR < ns) merge_word(bits[bb()]);
+                            if (s0 + bb() * TPR < ns) merge_word(mm, ll, bits[bb()]);
                         });
                     }
                 }
-                const float fin = finish_row();
+#pragma unroll
+                for (int o = 1; o < TPR; o <<= 1) {
+                    const float m2 = __shfl_xor(mm, o, TPR);
+                    const float l2 = __shfl_xor(ll, o, TPR);
+                    merge_stats(mm, ll, m2, l2, 1.f);
+                }
+                const float fin = row_m < p.M && ll > 0.f ? mm + __builtin_amdgcn_logf(ll) : __builtin_huge_valf();
                 if (sub == 0) {
                     sh_fin[row_m] = fin;
                     if (row_m < p.M) st_ag(&fin_slot[row_m], ~__float_as_uint(fin));
@@ -354,15 +372,13 @@ obs_onepass_kernel(const StreamParams p) {
                 }
                 sh_fin[tid] = fin;
             }
-        }
-        __syncthreads();
-        // The segment is complete: draw the next item, and count this item's read of the slots
-        // (short segments) or of the shifts (long ones).  Both round trips overlap the votes.
-        uint32_t next = 0, read_before = 0;
-        if (tid == 0) {
-            next = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (self_merge || !last_item)
-                read_before = __hip_atomic_fetch_add(readers, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            // The segment is complete: draw the next item; count this item's read of the shifts
+            // (the ns - 1 items other than the merger read them).  Both overlap the votes.
+            if (tid == 0) {
+                next = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (!last_item) read_before = __hip_atomic_fetch_add(readers, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
 
         // ---- votes: resident weights x row factor, summed over the 32 rows ----
@@ -386,21 +402,34 @@ obs_onepass_kernel(const StreamParams p) {
         }
 
         // ---- the last reader clears the segment's slots (and shifts) for the next launch ----
-        if (tid == 0) {
-            // short segments: ns readers; long: the ns - 1 that read the published shifts
-            const uint32_t n_readers = self_merge ? (uint32_t)ns : (uint32_t)ns - 1;
-            const bool clear = (self_merge || !last_item) ? read_before + 1 == n_readers : ns == 1;
-            if (clear) st_ag(readers, 0u);
-            if (!self_merge && last_item) st_ag(done_ctr, 0u);
-            sh_flag = clear ? 1 : 0;
-            sh_ticket = (int)next;
-        }
-        __syncthreads();
-        if (sh_flag) {
-            for (int k = tid; k < ns * MROWS; k += NT)
-                __hip_atomic_store(&slots[(int64_t)item0 * MROWS + k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (!self_merge)
+        if (self_merge) {
+            // ns readers (wave 0 of each item); the last clears with its own wave
+            if (wave == 0) {
+                const bool clear = __builtin_amdgcn_readfirstlane((int)read_before) + 1 == ns;
+                if (clear) {
+                    if (lane == 0) st_ag(readers, 0u);
+                    for (int k = lane; k < ns * MROWS; k += 64)
+                        __hip_atomic_store(&slots[(int64_t)item0 * MROWS + k], 0ull, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (lane == 0) sh_ticket = (int)next;
+            }
+            __syncthreads();
+        } else {
+            if (tid == 0) {
+                // ns - 1 readers; with ns == 1 the merger clears
+                const bool clear = last_item ? ns == 1 : read_before + 1 == (uint32_t)ns - 1;
+                if (clear) st_ag(readers, 0u);
+                if (last_item) st_ag(done_ctr, 0u);
+                sh_flag = clear ? 1 : 0;
+                sh_ticket = (int)next;
+            }
+            __syncthreads();
+            if (sh_flag) {
+                for (int k = tid; k < ns * MROWS; k += NT)
+                    __hip_atomic_store(&slots[(int64_t)item0 * MROWS + k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 for (int k = tid; k < MROWS; k += NT) st_ag(&fin_slot[k], 0u);
+            }
         }
         const int t_next = sh_ticket;
         __syncthreads();  // everyone has read sh_ticket, sh_flag and sh_fin before they are written again
