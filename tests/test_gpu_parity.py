@@ -224,6 +224,7 @@ ONEPASS = [
     ("onepass_gqa_M32_f32_d64", [6000], 4, 2, 64, "f32", 16, 7, None, 200, 8, 0),
     ("onepass_prefix_only", [9000, 1500], 4, 4, 128, "bf16", 32, 7, 0.05, None, 8, 1),
     ("onepass_245_items", [500000], 1, 1, 128, "bf16", 32, 7, 0.05, None, 64, 0),
+    ("onepass_32_items_self_merge", [65536, 65537], 2, 2, 128, "bf16", 32, 7, 0.05, None, 16, 0),
 ]
 
 
@@ -531,6 +532,45 @@ def test_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(a["idx"], b["idx"]) and torch.equal(a["pooled"], b["pooled"])
     assert torch.equal(a["K_out"], b["K_out"]) and torch.equal(a["V_out"], b["V_out"])
+
+
+# One workspace across calls on different inputs of one shape: every counter, flag and tagged
+# slot a call uses must be back at zero for the next call, or the next call's votes come out
+# wrong (stale row stats would be taken as this call's).
+WS_REUSE = [
+    # name, lengths, Hq, Hkv, flags
+    ("onepass_short_segments", [20000, 7000], 4, 4, {}),
+    ("onepass_long_segment", [80000], 2, 2, {}),
+    ("stream_gqa", [20000, 7000], 16, 4, {}),
+    ("stream_mha_forced", [30000], 4, 4, {"stream": True}),
+    ("fused_forced", [20000, 3000], 4, 4, {"fused": True}),
+]
+
+
+@pytest.mark.parametrize("case", WS_REUSE, ids=[c[0] for c in WS_REUSE])
+def test_workspace_reuse_across_inputs(case):
+    name, lengths, Hq, Hkv, flags = case
+    snap = _snap()
+    wl = synth.custom(lengths, Hq, Hkv, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8, name=name)
+    ws = None
+    for layer in (0, 1, 0):
+        _say("case %s layer %d" % (name, layer))
+        x = synth.make_inputs(wl, layer, threads=16)
+        q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+        cu = x["cu_seqlens"]
+        spec = snap.make_spec(q, K, cu, 32, 7, 0.05, None, **flags)
+        if ws is None:
+            ws = snap.workspace(spec, K.device)
+        res = snap.compress(q, K, V, cu, obs_window=32, pool_kernel=7, ratio=0.05, want_pooled=True, ws=ws, **flags)
+        torch.cuda.synchronize()
+        ref = oracle.compress(x["q_obs"], x["K"], x["V"], cu, 32, 7, ratio=0.05, with_gather=False)
+        pooled, idx = res["pooled"].cpu().numpy(), res["idx"].cpu().numpy()
+        for (r, g), rr in sorted(ref.items()):
+            tag = "%s layer %d r=%d g=%d" % (name, layer, r, g)
+            cols = slice(int(spec.cu_pfx[r]), int(spec.cu_pfx[r + 1]))
+            check_scores(pooled[g, cols], rr["pooled"], tag + " pooled")
+            check_selection(idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])], rr["pooled"], rr["idx"], rr["k"],
+                            tag + " select")
 
 
 def test_workspace_counters_left_zero():
