@@ -39,10 +39,10 @@ METRIC = "prompt tokens compressed/s per layer + % peak HBM GB/s (Llama-7B shape
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E, AMD public specification
 CACHE_BYTES = 256 << 20          # MI355X Infinity Cache
 KERNEL_SOURCES = ("kv_cache_compression_amd/csrc/obs_score.hip", "kv_cache_compression_amd/csrc/obs_score_kernel.h",
-                  "kv_cache_compression_amd/csrc/obs_stream.hip", "kv_cache_compression_amd/csrc/obs_onepass.hip")
-SCORING_KERNELS = ("obs_score_onepass", "obs_score_fused", "obs_score_stream", "obs_score_stats", "obs_stats_merge",
-                   "obs_score_votes",
-                   "sum_chunks")
+                  "kv_cache_compression_amd/csrc/obs_stream.hip", "kv_cache_compression_amd/csrc/obs_onepass.hip",
+                  "kv_cache_compression_amd/csrc/obs_onepass2.hip")
+SCORING_KERNELS = ("obs_score_onepass", "obs_score_onepass2", "obs_score_fused", "obs_score_stream", "obs_score_stats",
+                   "obs_stats_merge", "obs_score_votes", "sum_chunks")
 
 
 def parse():
@@ -147,7 +147,8 @@ def profiled_traffic(workload_name):
 
 def scoring_name(kernels_us):
     """Which scoring path a run took, from the kernels it launched."""
-    for name, tag in (("obs_score_onepass", "one_read_stream"), ("obs_score_fused", "fused"),
+    for name, tag in (("obs_score_onepass", "one_read_stream"), ("obs_score_onepass2", "one_read_two_slots"),
+                      ("obs_score_fused", "fused"),
                       ("obs_score_stream", "two_phase_stream"), ("obs_score_stats", "two_pass")):
         if name in kernels_us:
             return tag
@@ -398,7 +399,8 @@ class Run:
             dom = max(scoring, key=scoring.get)
             n_l = launches.get(dom, 1.0) or 1.0
             res["dominant"] = dom
-            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_onepass", "obs_score_fused",
+            res["dominant_alg_bytes_per_launch"] = obs_bytes / n_l if dom in ("obs_score_onepass", "obs_score_onepass2",
+                                                                            "obs_score_fused",
                                                                             "obs_score_stream",
                                                                             "obs_score_votes") else None
             res["dominant_launch_us"] = launch_us[dom]

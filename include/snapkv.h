@@ -83,10 +83,14 @@ typedef enum { SNAPKV_CAUSAL_WINDOW = 0, SNAPKV_PREFIX_ONLY = 1 } snapkv_variant
                                      and the lse calls) */
 #define SNAPKV_FLAG_FUSED 0x4u    /* score with the fused barrier kernel (logits resident, one grid
                                      iteration per set of whole segments).  Without a flag, rows of
-                                     256 bytes with G * L_obs <= 32 use the streaming one-read kernel
-                                     (its longest segment must fit the resident grid: 256 slabs of
-                                     2048 keys on an MI355X, i.e. 524288 tokens), then the fused
-                                     kernel, then two passes.  The three flags exclude each other. */
+                                     256 bytes with G * L_obs <= 32 use a one-read kernel: the
+                                     single-slot one when the group's 2048-key items fit one pass of
+                                     the resident grid (256 workgroups on an MI355X), else the
+                                     two-slot one when no segment has more than twice the grid's
+                                     1024-key items (524288 tokens), else the two-phase kernel; other
+                                     problems use the two-phase kernel when it takes them, then the
+                                     fused kernel, then two passes.  The three flags exclude each
+                                     other. */
 
 typedef struct {
     int32_t batch;            /* B >= 1 requests */
@@ -290,7 +294,9 @@ typedef enum {
     SNAPKV_K_HIT_CLEAR = 13,      /* snapkv_hit_rate: zeroes the counts its tiles add to */
     SNAPKV_K_SCRATCH_CLEAR = 14,  /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
     SNAPKV_K_OBS_STREAM = 15,     /* obs_score, streaming two-phase kernel (work tickets, no barrier) */
-    SNAPKV_K_OBS_ONEPASS = 16     /* obs_score, streaming one-read kernel (<= 32 rows, weights resident) */
+    SNAPKV_K_OBS_ONEPASS = 16,    /* obs_score, streaming one-read kernel (<= 32 rows, weights resident) */
+    SNAPKV_K_OBS_ONEPASS2 = 17    /* obs_score, one-read kernel with two items in flight per workgroup
+                                     (<= 32 rows, long segments) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -454,6 +454,9 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
     int op_threads = 0, op_slab = 0;
     const void *ko = p.st_ok && p.st_rows == 32 ? onepass_kernel(p.dtype, &op_threads, &op_slab) : nullptr;
     const int op_grid = ko ? occupancy(ko, op_threads) * di.cus : 0;
+    int o2_threads = 0, o2_slab = 0;
+    const void *ko2 = ko ? onepass2_kernel(p.dtype, &o2_threads, &o2_slab) : nullptr;
+    const int o2_grid = ko2 ? occupancy(ko2, o2_threads) * di.cus : 0;
     const bool forced = (p.flags & (SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED)) != 0;
     for (const Group &gr : p.groups) {
         int max_ns = 0;
@@ -468,17 +471,23 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
         // is faster (825 against 965 us at the 380K-token layer).  Grouped-query heads and the
         // caller's row stats: the two-phase kernel too (it reads each key once per pass for all
         // of a group's rows).  Otherwise the fused kernel, else two passes.
+        int o2_max_ns = 0;
+        const int64_t o2_items = ko2 ? stream_items(p, gr, o2_slab, &o2_max_ns) : 0;
         const bool use_onepass = ko && !lse && !forced && op_grid > 0 && op_items <= op_grid && op_max_ns <= op_grid;
-        const bool use_stream = !use_onepass && p.st_ok && st_grid > 0 && !(p.flags & SNAPKV_FLAG_FUSED) &&
+        const int o2_launch = o2_items < o2_grid ? (int)o2_items : o2_grid;
+        const bool use_onepass2 = !use_onepass && ko2 && !lse && !forced && o2_launch > 0 &&
+                                  o2_max_ns <= 2 * o2_launch;
+        const bool use_stream = !use_onepass && !use_onepass2 && p.st_ok && st_grid > 0 && !(p.flags & SNAPKV_FLAG_FUSED) &&
                                 !(p.flags & SNAPKV_FLAG_TWO_PASS);
-        if (use_onepass || use_stream) {
+        const bool one_read = use_onepass || use_onepass2;
+        if (one_read || use_stream) {
             StreamParams sp;
             memset(&sp, 0, sizeof sp);
             sp.q = q;
             sp.K = K;
             sp.votes = votes;
-            sp.partial = (float2 *)(ws + (use_onepass ? p.off_op_partial : p.off_st_partial));
-            sp.final_shift = (float *)(ws + (use_onepass ? p.off_op_final : p.off_st_final));
+            sp.partial = (float2 *)(ws + (one_read ? p.off_op_partial : p.off_st_partial));
+            sp.final_shift = (float *)(ws + (one_read ? p.off_op_final : p.off_st_final));
             sp.ticket = (uint32_t *)(ws + p.off_st_ticket);
             sp.seg_ctl = (uint32_t *)(ws + p.off_st_ctl);
             sp.err = err;
@@ -496,7 +505,7 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
             sp.c = (float)(1.4426950408889634 / sqrt((double)p.d));
             // the one-read kernel always takes its largest slab: it runs every step of an item
             // whatever the slab's length
-            const int slab_keys = use_onepass ? op_slab : p.st_slab;
+            const int slab_keys = use_onepass ? op_slab : use_onepass2 ? o2_slab : p.st_slab;
             sp.slab_keys = slab_keys;
             sp.spin_limit = kSpinLimit;
             sp.rt = gr.rt;
@@ -510,6 +519,8 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
             if (use_onepass) {
                 const int grid = n < op_grid ? (int)n : op_grid;
                 st = launch(SNAPKV_K_OBS_ONEPASS, ko, dim3(grid), dim3(op_threads), &sp, stream);
+            } else if (use_onepass2) {
+                st = launch(SNAPKV_K_OBS_ONEPASS2, ko2, dim3(o2_launch), dim3(o2_threads), &sp, stream);
             } else {
                 // Votes items trail the stats items of their segment by about one pass of the grid:
                 // close enough that part of the second read still comes from the Infinity Cache,
@@ -1151,6 +1162,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
         case SNAPKV_K_OBS_STREAM: return "obs_score_stream";
         case SNAPKV_K_OBS_ONEPASS: return "obs_score_onepass";
+        case SNAPKV_K_OBS_ONEPASS2: return "obs_score_onepass2";
         default: return "unknown";
     }
 }

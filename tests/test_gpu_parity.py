@@ -243,6 +243,55 @@ def test_onepass_kernel(case):
     run_and_check(wl, variant=variant, token_major=True, inputs=x)
 
 
+# The one-read kernel with two items in flight per workgroup (the default for up to 32 rows of
+# 256 bytes per KV head when a layer's 2048-key items exceed one pass of the resident grid and
+# no segment has more than twice the grid's 1024-key items): segments merged per item (at most
+# 32 items) and through the published shifts, mixed in one launch, grouped heads of 32 rows,
+# fp32, the prefix-only variant, a request with an empty prefix, and a segment of exactly twice
+# the grid's items (the longest it takes; one token more goes to the two-phase kernel).
+ONEPASS2 = [
+    # name, lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant, variant
+    ("onepass2_central_merge", [300000], 2, 2, 128, "bf16", 32, 13, 0.05, None, 64, 0),
+    ("onepass2_self_merge", [30000, 20000, 25000, 9000, 33, 1500], 8, 8, 128, "bf16", 32, 7, 0.05, None, 16, 0),
+    ("onepass2_mixed", [45000, 3000, 20000, 700], 8, 8, 128, "bf16", 32, 7, 0.05, None, 16, 0),
+    ("onepass2_gqa_M32", [70000, 3000], 16, 8, 128, "bf16", 16, 7, 0.05, None, 16, 0),
+    ("onepass2_f32_d64", [40000, 30000], 8, 8, 64, "f32", 32, 5, None, 1000, 16, 0),
+    ("onepass2_prefix_only", [70000, 1500, 32], 8, 8, 128, "bf16", 32, 7, 0.05, None, 16, 1),
+]
+
+
+def _device_cus():
+    return int(torch.cuda.get_device_properties(0).multi_processor_count)
+
+
+def _check_onepass2(name, lengths, Hq, Hkv, d, dt, w, kp, ratio, budget, n_plant, variant, expect=17):
+    wl = synth.custom(lengths, Hq, Hkv, d, dtype=dt, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget,
+                      n_plant=n_plant, name=name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    snap = _snap()
+    q, K = to_torch(x["q_obs"]), to_torch(x["K"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, variant=variant)
+    ids = _launched_kernels(lambda: snap.scores(q, K, x["cu_seqlens"], **kw))
+    assert expect in ids and 16 not in ids and 1 not in ids, "expected scoring kernel %d, launched %s" % (expect, ids)
+    run_and_check(wl, variant=variant, inputs=x)
+    if expect == 17:
+        run_and_check(wl, variant=variant, token_major=True, inputs=x)
+
+
+@pytest.mark.parametrize("case", ONEPASS2, ids=[c[0] for c in ONEPASS2])
+def test_onepass2_kernel(case):
+    _check_onepass2(*case)
+
+
+@pytest.mark.parametrize("extra", [0, 1], ids=["twice_the_grid", "one_token_more"])
+def test_onepass2_segment_limit(extra):
+    """A segment of 2 * grid 1024-key items takes the two-slot kernel; one token more, the
+    two-phase streaming kernel (a segment must fit in both slots of the resident grid)."""
+    L = 2 * _device_cus() * 1024 + extra
+    _check_onepass2("onepass2_limit_%d" % extra, [L], 2, 2, 128, "bf16", 32, 7, 0.05, None, 64, 0,
+                    expect=17 if extra == 0 else 15)
+
+
 # Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
 # positions per thread of 1024) and past the 32768 positions it holds on chip.
 SELECT_P = [1, 2, 3, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 70001]
@@ -541,6 +590,7 @@ WS_REUSE = [
     # name, lengths, Hq, Hkv, flags
     ("onepass_short_segments", [20000, 7000], 4, 4, {}),
     ("onepass_long_segment", [80000], 2, 2, {}),
+    ("onepass2_two_slots", [300000, 40000, 5000], 2, 2, {}),
     ("stream_gqa", [20000, 7000], 16, 4, {}),
     ("stream_mha_forced", [30000], 4, 4, {"stream": True}),
     ("fused_forced", [20000, 3000], 4, 4, {"fused": True}),
