@@ -313,8 +313,19 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     // one-read scoring (32 rows): per-item row stats and per-segment row shifts, both tagged so
     // that zero means "not yet written"; every call leaves them at zero
     const bool op_ok = p.st_ok && p.st_rows == 32;
+    int64_t op_max_items = 0;  // items of the largest group at the one-read kernels' smallest slab
+    if (op_ok) {
+        int thr = 0, slab1 = 0, slab2 = 0;
+        (void)onepass_kernel(p.dtype, &thr, &slab1);
+        (void)onepass2_kernel(p.dtype, &thr, &slab2);
+        const int slab = slab1 < slab2 ? slab1 : slab2;
+        for (const Group &gr : p.groups) {
+            const int64_t n = stream_items(p, gr, slab, nullptr);
+            op_max_items = n > op_max_items ? n : op_max_items;
+        }
+    }
     p.off_op_partial = off;
-    if (op_ok) off = align_up(off + sizeof(float) * 2 * 32 * (size_t)p.st_max_items);
+    if (op_ok) off = align_up(off + sizeof(uint64_t) * 32 * (size_t)op_max_items);
     p.off_op_final = off;
     if (op_ok) off = align_up(off + sizeof(float) * 32 * (size_t)p.max_group_segs);
     p.ws_bytes = off;
@@ -516,6 +527,8 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
             }
             sp.rt.slab0[gr.rt.n] = (int32_t)n;
             sp.n_items = (int32_t)n;
+            if (one_read && (size_t)n * 32 * sizeof(uint64_t) > p.off_op_final - p.off_op_partial)
+                return fail(SNAPKV_EUNSUPPORTED, "one-read stats region smaller than the launch's items");
             if (use_onepass) {
                 const int grid = n < op_grid ? (int)n : op_grid;
                 st = launch(SNAPKV_K_OBS_ONEPASS, ko, dim3(grid), dim3(op_threads), &sp, stream);

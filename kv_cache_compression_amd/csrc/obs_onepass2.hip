@@ -10,23 +10,28 @@
 // How it maps to CDNA4.  As the one-read kernel (obs_onepass.hip): each wave scores its own
 // 16-key tile per step for all 32 rows and keeps the exponentials in VGPRs; the items of a
 // segment exchange per-row (shift, sum) through tagged slots.  The difference: a workgroup holds
-// two items of 1024 keys (two register slots of 64 exponentials per lane each).  Once an item is
-// scored and its stats published, the workgroup draws and scores the next item into the other
-// slot, and only then finishes the first (waits for its segment, writes its votes).  So the wait
-// of an item for the rest of its segment overlaps the key stream of the next, which matters when
-// a segment's items are a large part of the grid (at the 380K-token layer each segment needs 372
-// items): the single-slot kernel there spends more time waiting than streaming.
+// two items of 1024 keys (two register slots of 64 exponentials per lane each).  It scores an
+// item into the free slot and publishes its stats, then finishes the older item (waits for its
+// segment, writes its votes).  So the wait of an item for the rest of its segment overlaps the
+// key stream of the next, which matters when a segment's items are a large part of the grid (at
+// the 380K-token layer each segment has 372 items): the single-slot kernel there spends more
+// time waiting than streaming.
+// Items are dealt round robin (workgroup w of G takes items w, w + G, w + 2G, ...), so the next
+// item is known early: its query rows (copied to LDS by the buffer unit, no registers) and its
+// first key steps are issued before the older item is finished, and the memory pipe keeps
+// streaming through the wait and the votes.  The barriers order LDS only, so those loads stay
+// in flight across them.  The MFMA query operand is read from the LDS tile at each step, which
+// keeps the registers of both slots, the keys in flight and the step's operands within 256.
 // Meeting the segment: short segments (at most kSelfMergeItems items) merge per item, as in the
-// one-read kernel.  In a longer segment the item with the highest index, which is drawn after
-// all of the segment's other items, polls their tagged stats, merges them and publishes the row
-// shifts; the others poll those.  So no item of a long segment takes an arrival count.
+// one-read kernel.  In a longer segment the item with the highest index polls the other items'
+// tagged stats, merges them and publishes the row shifts; the others poll those.  So no item of
+// a long segment takes an arrival count.
 // Waits: a workgroup blocks only on the older of its two items (after scoring the younger), and
-// a segment's last item on the segment's other items, which are drawn before it and published
-// without waiting.  So the launch completes whenever a segment's items fit in twice the resident
-// grid, which the host checks (a blocked grid's slots would all hold items of the one segment
-// that straddles the next ticket).  Tickets are drawn once the older item's segment is complete;
-// the reader counts that let a segment's last reader clear its stats or shifts are looked at a
-// finish later, off the path.  Every counter and tagged slot is back at zero when the launch ends.
+// a segment's last item on the segment's other items.  Item j is scored once its workgroup has
+// finished item j - 2G, which lies in an earlier segment when a segment has at most 2G items
+// (checked by the host); so by induction over segments every wait ends.  The reader counts that
+// let a segment's last reader clear its stats or shifts are looked at a finish later, off the
+// path.  Every counter and tagged slot is back at zero when the launch ends.
 // Exponentials are base 2: s*log2(e)/sqrt(d) with the scale folded into one FMA.
 #include "obs_score_kernel.h"
 
@@ -38,6 +43,14 @@ constexpr float kSumTop = 1.26765060022823e30f;  // 2^100
 constexpr int kRaises = 8;                       // re-scorings of a wave-row whose sum overflows
 constexpr int kSelfMergeItems = 32;              // segments of up to this many items merge per item
 constexpr uint32_t kSumTag = 0x80000000u;        // set in a published row sum (sums are >= +0)
+
+// Workgroup barrier that orders LDS only: vector memory operations in flight (prefetched key
+// rows) are not waited for, unlike __syncthreads.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ inline uint32_t ld_ag2(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -67,13 +80,15 @@ obs_onepass2_kernel(const StreamParams p) {
     constexpr int TPR = NT / MROWS;  // threads per row in the central merge
     static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0, "threads per row");
     static_assert(MROWS == 32, "a wave polls two items per row per load round");
+    static_assert(NT == MROWS * 16, "one 16-byte query chunk per thread");
 
     __shared__ u32x4_t sh_k[NW][256];        // each wave's staging tile (no other wave touches it)
     __shared__ float sh_ms[NW][MROWS], sh_ml[NW][MROWS];
     __shared__ float sh_lsh[2][NW][MROWS];   // per slot: each wave's row shifts (-inf: no weights)
     __shared__ float sh_fin[2][MROWS];       // per slot: segment row shifts, +inf for padding rows
+    __shared__ u32x4_t sh_q[MROWS * 16];     // the next item's query rows (slot 16 row + (chunk ^ row % 16))
     __shared__ int sh_wrow[MROWS];
-    __shared__ int sh_ticket, sh_flag;
+    __shared__ int sh_flag;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -84,6 +99,7 @@ obs_onepass2_kernel(const StreamParams p) {
     uint64_t *const slots = (uint64_t *)p.partial;  // [item][32]: (shift, sum | kSumTag), 0 = unwritten
 
     for (int r = tid; r < MROWS; r += NT) sh_wrow[r] = r % p.w;
+    sh_q[tid] = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
 
     auto decode = [&](int item) {
@@ -107,51 +123,73 @@ obs_onepass2_kernel(const StreamParams p) {
     };
     auto ctl = [&](int seg, int line) { return p.seg_ctl + (int64_t)seg * 3 * kStreamSegLine + line * kStreamSegLine; };
     auto fin_slot = [&](int seg) { return (uint32_t *)p.final_shift + (int64_t)seg * MROWS; };
-    auto draw = [&]() {
-        if (tid == 0) sh_ticket = (int)gridDim.x + (int)__hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const int t = sh_ticket;
-        __syncthreads();
-        // N draws in all (one per item after the first of each workgroup, one past the end per
-        // workgroup); the last resets the counter for the next launch
-        if (tid == 0 && t == N - 1 + (int)gridDim.x) st_ag2(p.ticket, 0u);
-        return t;
+    float E[2][RES][RTW][4];
+    u32x4_t kreg[DEPTH][4];  // key rows in flight (the first DEPTH steps of an item can be prefetched)
+    const int row4 = 4 * (int)tstride;
+
+    auto item_rsrc = [&](const Item2 &it) {
+        const char *slab_base =
+            (const char *)p.K + ((int64_t)it.g * p.head_stride + (p.rt.tok0[it.r] + it.key0) * p.token_stride) * ESZ;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)slab_base, (short)0, (int)(it.nkeys * tstride), kBufferFlags);
+    };
+    auto item_lane_off = [&](int tl) { return ((tl >> 6) * 16 + ((tl >> 4) & 3)) * (int)tstride + (tl & 15) * 16; };
+    // The item's query rows and its first DEPTH steps of keys, issued before the workgroup
+    // finishes its older item, so that the key stream does not stop while it waits and votes.
+    auto issue_first = [&](const int item) {
+        const Item2 it = decode(item);
+        const int tl = opaque((int)threadIdx.x);
+        // query rows -> LDS without passing through registers: lane l of wave v fills tile slot
+        // 64v + l, i.e. row (64v + l) / 16, chunk ((64v + l) % 16) ^ row % 16; rows past M are
+        // out of the buffer's range
+        {
+            const char *qb = (const char *)p.q + (((int64_t)p.rt.qi[it.r] * p.Hq + (int64_t)it.g * p.G) * (int64_t)p.w) * ROWB;
+            const __amdgpu_buffer_rsrc_t qrsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)qb, (short)0, p.M * ROWB, kBufferFlags);
+            const int slot = tl & (NT - 1);
+            const int qrow = slot >> 4, qch = (slot & 15) ^ (qrow & 15);
+            const int vw = __builtin_amdgcn_readfirstlane(tl >> 6);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void *)&sh_q[64 * vw], 16,
+                                                     qrow * ROWB + qch * 16, 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");  // the copy is issued before the key loads
+        const __amdgpu_buffer_rsrc_t rsrc = item_rsrc(it);
+        const int lane_off = item_lane_off(tl);
+        int lbase = 0;
+        static_for<DEPTH>([&](auto bc) {
+            constexpr int B = decltype(bc)::value;
+            asm volatile("" : "+s"(lbase));
+            static_for<4>([&](auto i) {
+                kreg[B][i] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane_off + lbase + i * row4, 0, kNonTemporal));
+            });
+            lbase += kStepKeys * (int)tstride;
+        });
     };
 
-    float E[2][RES][RTW][4];
-    u32x4_t qf[RTW][NQ];
-
-    // ---- score an item into slot SL and publish its row stats (long segments: arrive) ----
-    auto stream_item = [&](auto slot_c, Item2 &it) {
+    // ---- score an item into slot SL and publish its row stats ----
+    auto stream_item = [&](auto slot_c, const int item) {  // issue_first(item) has been called
+        const Item2 it = decode(item);
         constexpr int SL = decltype(slot_c)::value;
-        const int r = it.r, g = it.g, P = it.P, key0 = it.key0, nkeys = it.nkeys;
+        const int P = it.P, key0 = it.key0, nkeys = it.nkeys;
         // lane indices re-derived per item from an opaque thread index: nothing lane-dependent
         // is hoisted out of the item loop into registers held beside both slots' weights
         const int tid = opaque((int)threadIdx.x), tl = tid;
         const int wave = tl >> 6, n16 = tl & 15, grp = (tl >> 4) & 3;
         const int lrow = grp, lch = n16;
-        const int lane_off = (wave * 16 + lrow) * (int)tstride + lch * 16;
+        const int lane_off = item_lane_off(tl);
         u32x4_t *const stile = sh_k[wave];
-        {
-            const char *qb = (const char *)p.q + (((int64_t)p.rt.qi[r] * p.Hq + (int64_t)g * p.G) * (int64_t)p.w) * ROWB;
-            static_for<RTW>([&](auto rt) {
-                const int row = rt * 16 + n16;
-                static_for<NQ>([&](auto qq) {
-                    qf[rt][qq] = row < p.M ? *(const u32x4_t *)(qb + (int64_t)row * ROWB + (4 * qq + grp) * 16)
-                                           : u32x4_t{0u, 0u, 0u, 0u};
-                });
-            });
-        }
-        const char *slab_base = (const char *)p.K + ((int64_t)g * p.head_stride + (p.rt.tok0[r] + key0) * p.token_stride) * ESZ;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc((void *)slab_base, (short)0, (int)(nkeys * tstride), kBufferFlags);
+        // the query rows staged by issue_first (every wave's part): wait for this wave's copy,
+        // then for the others'
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        const __amdgpu_buffer_rsrc_t rsrc = item_rsrc(it);
         const int vis_end = P < key0 + nkeys ? P : key0 + nkeys;
         float lsh[RTW][4], lw[RTW][4];
         // Every step runs (no branch around a step or a load); loads past the slab read zeros.
+        // first: the first scoring of the item (its first steps are in flight already); later
+        // ones (raised shifts) load them again
         auto score = [&](const bool first) {
-            u32x4_t kreg[DEPTH][4];
-            int lbase = 0;
-            const int row4 = 4 * (int)tstride;
+            int lbase = first ? DEPTH * kStepKeys * (int)tstride : 0;
             auto load_step = [&](auto bc) {
                 constexpr int B = decltype(bc)::value;
                 asm volatile("" : "+s"(lbase));
@@ -161,7 +199,7 @@ obs_onepass2_kernel(const StreamParams p) {
                 });
                 lbase += kStepKeys * (int)tstride;
             };
-            static_for<DEPTH>([&](auto j) { load_step(j); });
+            if (!first) static_for<DEPTH>([&](auto j) { load_step(j); });
             const int tail = vis_end - key0;
             static_for<RES>([&](auto sc) {
                 constexpr int s = decltype(sc)::value;
@@ -176,7 +214,11 @@ obs_onepass2_kernel(const StreamParams p) {
                 f32x4_t S[RTW];
                 static_for<RTW>([&](auto rt) {
                     S[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    static_for<NQ>([&](auto qq) { S[rt] = Dot<T>::step(qf[rt][qq], kf[qq], S[rt]); });
+                    static_for<NQ>([&](auto qq) {
+                        // query operand read from the LDS tile at each step (no registers held)
+                        const u32x4_t qv = sh_q[16 * (rt * 16 + n16) + ((4 * qq + grp) ^ n16)];
+                        S[rt] = Dot<T>::step(qv, kf[qq], S[rt]);
+                    });
                 });
                 if ((s + 1) * kStepKeys > opaque_s(tail)) {
                     const int t = opaque(tid);
@@ -249,7 +291,7 @@ obs_onepass2_kernel(const StreamParams p) {
                 }
             });
         });
-        __syncthreads();
+        lds_barrier();
         if (tid < MROWS && tid < p.M) {
             const int row = tid;
             float m = sh_ms[0][row];
@@ -264,9 +306,8 @@ obs_onepass2_kernel(const StreamParams p) {
             __hip_atomic_store(&slots[(int64_t)it.item * MROWS + row], word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (it.last) {
-            // The segment's last item (drawn after all of its other items, which the workgroups
-            // holding them publish without waiting): poll every item's tagged stats, merge
-            // them, publish the row shifts, and clear the stats (this item is their only reader).
+            // The segment's last item: poll every item's tagged stats, merge them, publish the
+            // row shifts, and clear the stats (this item is their only reader).
             const int row_m = tid / TPR, sub = tid - (tid / TPR) * TPR;
             float mm = neg_inf(), ll = 0.f;
             if (row_m < p.M) {
@@ -309,18 +350,16 @@ obs_onepass2_kernel(const StreamParams p) {
                 sh_fin[SL][row_m] = fin;
                 if (row_m < p.M) st_ag2(&fin_slot(it.seg)[row_m], ~__float_as_uint(fin));
             }
-            __syncthreads();  // every thread's loads of the stats are done
+            lds_barrier();  // every thread's loads of the stats are done
             for (int k = tid; k < it.ns * MROWS; k += NT)
                 __hip_atomic_store(&slots[(int64_t)it.item0 * MROWS + k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
 
     // ---- wait for an item's segment and write the votes of slot SL ----
-    // With do_draw, the next ticket is drawn once the segment is complete (the draw's round trip
-    // overlaps the votes) and returned.  The item's reader count is taken at the same point;
-    // its value is looked at in the workgroup's next finish (or at exit), where the segment's
-    // last reader clears the stats (short segments) or the shifts (long ones): nothing waits
-    // for that round trip.
+    // The item's reader count is taken once its segment is complete; its value is looked at in
+    // the workgroup's next finish (or at exit), where the segment's last reader clears the stats
+    // (short segments) or the shifts (long ones): nothing waits for that round trip.
     int pend_item0 = 0, pend_ns = 0, pend_seg = 0, pend_kind = 0;  // kind 0: none, 1: short, 2: long
     uint32_t pend_rb = 0;                                          // thread 0: readers before it
     auto pending_clear_flag = [&]() {
@@ -339,7 +378,8 @@ obs_onepass2_kernel(const StreamParams p) {
             for (int k = tid; k < MROWS; k += NT) st_ag2(&fin_slot(pend_seg)[k], 0u);
         }
     };
-    auto finish_item = [&](auto slot_c, const Item2 &it, const bool do_draw) {
+    auto finish_item = [&](auto slot_c, const int item) {
+        const Item2 it = decode(item);
         constexpr int SL = decltype(slot_c)::value;
         const int tid = opaque((int)threadIdx.x), tl = tid;
         const int lane = tl & 63, wave = tl >> 6, n16 = tl & 15, grp = (tl >> 4) & 3;
@@ -395,16 +435,13 @@ obs_onepass2_kernel(const StreamParams p) {
             }
             sh_fin[SL][tid] = fin;
         }
-        __syncthreads();
-        // the segment is complete: draw, and count this item's read (short segments: of the
-        // stats, ns readers; long: of the shifts, the ns - 1 items other than the last);
-        // issued after the barrier, whose release fence would otherwise wait for them
-        uint32_t tk = 0;
+        lds_barrier();
+        // the segment is complete: count this item's read (short segments: of the stats, ns
+        // readers; long: of the shifts, the ns - 1 items other than the last); issued after the
+        // barrier, whose release fence would otherwise wait for it
         const bool counted = self_merge || !it.last;
-        if (tid == 0) {
-            if (do_draw) tk = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (counted) pend_rb = __hip_atomic_fetch_add(ctl(it.seg, 2), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tid == 0 && counted)
+            pend_rb = __hip_atomic_fetch_add(ctl(it.seg, 2), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (sh_flag) pending_clear(tid);
         pend_kind = counted ? (self_merge ? 1 : 2) : 0;
         pend_item0 = it.item0;
@@ -429,40 +466,34 @@ obs_onepass2_kernel(const StreamParams p) {
                 if (grp == 0 && j < vis_end) vout[j] = v;
             });
         }
-        if (tid == 0 && do_draw) sh_ticket = (int)gridDim.x + (int)tk;
-        __syncthreads();  // sh_ticket is written; sh_flag, sh_fin and sh_lsh of this slot are free again
-        const int t = do_draw ? sh_ticket : N;
-        // N draws in all (one per item after the first of each workgroup, one past the end per
-        // workgroup); the last resets the counter for the next launch
-        if (tid == 0 && do_draw && t == N - 1 + (int)gridDim.x) st_ag2(p.ticket, 0u);
-        return t;
+        lds_barrier();  // sh_flag, sh_fin and sh_lsh of this slot are free again
     };
 
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    // Slot 0 and slot 1 alternate: score the next item into the free slot, then finish the
-    // older one (drawing the next ticket there).  The first item of a workgroup is its own index
-    // (the grid has at most N workgroups); the second is drawn right after the first is scored.
-    Item2 a = decode(blockIdx.x), b = a;
-    stream_item(S0{}, a);
-    int tb = draw();
+    // Items are dealt round robin: workgroup w takes items w, w + G, w + 2G, ... (G workgroups,
+    // at most N), slot 0 and slot 1 in turn.  Each item's queries and first keys are issued
+    // before the workgroup finishes its older item.
+    const int G = (int)gridDim.x;
+    int ia = (int)blockIdx.x, ib = ia + G;
+    issue_first(ia);
+    stream_item(S0{}, ia);
+    if (ib < N) issue_first(ib);
     for (;;) {
-        if (tb < N) {
-            b = decode(tb);
-            stream_item(S1{}, b);
-        }
-        const int ta = finish_item(S0{}, a, tb < N);
-        if (tb >= N) break;
-        if (ta < N) {
-            a = decode(ta);
-            stream_item(S0{}, a);
-        }
-        tb = finish_item(S1{}, b, ta < N);
-        if (ta >= N) break;
+        if (ib < N) stream_item(S1{}, ib);
+        if (ib < N && ia + 2 * G < N) issue_first(ia + 2 * G);
+        finish_item(S0{}, ia);
+        if (ib >= N) break;
+        ia += 2 * G;
+        if (ia < N) stream_item(S0{}, ia);
+        if (ia < N && ib + 2 * G < N) issue_first(ib + 2 * G);
+        finish_item(S1{}, ib);
+        if (ia >= N) break;
+        ib += 2 * G;
     }
     // the last finish's reader count
     if ((int)threadIdx.x == 0) sh_flag = pending_clear_flag() ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     if (sh_flag) pending_clear((int)threadIdx.x);
 }
 
