@@ -709,7 +709,9 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
             if (st) return st;
         }
         const bool any_k = p.cu_k[gr.rt.qi[gr.rt.n - 1] + 1] != p.cu_k[gr.rt.qi[0]];
-        if (any_k || (fuse && pooled)) {
+        bool any_resident = false;  // a segment the resident kernel takes (the others return at once)
+        for (int i = 0; i < gr.rt.n; ++i) any_resident = any_resident || gr.rt.L[i] - p.w <= select_lds_positions();
+        if (any_resident && (any_k || (fuse && pooled))) {
             SelectParams sp;
             memset(&sp, 0, sizeof sp);
             sp.votes = fuse ? votes : nullptr;
