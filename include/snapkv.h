@@ -123,7 +123,10 @@ typedef struct {
  *                       independent; 0 is never returned).
  * Workspace contract: zero-fill it once before its first use.  Every call
  * leaves its counters and tagged slots at zero again, so later calls (also
- * under graph replay) need no clearing.  The first 4 bytes hold a sticky error
+ * under graph replay) need no clearing.  Where they lie depends on the
+ * problem: a call whose counters lie elsewhere than those of the previous call
+ * on the same workspace (same address and device; another shape reusing it)
+ * first zeroes its own with one small kernel on its stream.  The first 4 bytes hold a sticky error
  * word that only the caller clears:
  *   bit 0 = a scoring workgroup gave up waiting for others of its launch.  The
  *           fused and the one-read kernels need all workgroups of a (request,
@@ -295,8 +298,9 @@ typedef enum {
     SNAPKV_K_SCRATCH_CLEAR = 14,  /* snapkv_compress_noalloc: zero-fills the device's array (first call) */
     SNAPKV_K_OBS_STREAM = 15,     /* obs_score, streaming two-phase kernel (work tickets, no barrier) */
     SNAPKV_K_OBS_ONEPASS = 16,    /* obs_score, streaming one-read kernel (<= 32 rows, weights resident) */
-    SNAPKV_K_OBS_ONEPASS2 = 17    /* obs_score, one-read kernel with two items in flight per workgroup
+    SNAPKV_K_OBS_ONEPASS2 = 17,   /* obs_score, one-read kernel with two items in flight per workgroup
                                      (<= 32 rows, long segments) */
+    SNAPKV_K_WS_CLEAR = 18        /* zeroes a workspace's counters when its layout changed */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <unordered_map>
 #include <string>
 #include <vector>
 
@@ -827,6 +828,68 @@ int scratch_for_device(hipStream_t stream, void **out) {
     return SNAPKV_OK;
 }
 
+// ---- control regions of a workspace --------------------------------------------------------
+// The ranges a call expects to find at zero: the fused kernel's arrival lines, the tile select's
+// per-segment state and histograms, the streaming kernels' ticket and control lines, and the
+// one-read kernels' tagged row stats and shifts.  Every call leaves them at zero again.  Their
+// offsets depend on the problem, so a call whose ranges differ from those of the previous call
+// on the same workspace (another shape reusing it) may find there the data the previous call
+// wrote (votes, indices, ...): such a call clears its ranges first, with one small kernel.
+struct CtlRange {
+    size_t off, bytes;
+};
+static int control_ranges(const Plan &p, CtlRange *r) {
+    int n = 0;
+    auto add = [&](size_t a, size_t b) {
+        if (b > a) r[n++] = CtlRange{a, b - a};
+    };
+    add(p.off_cnt, p.off_partial);         // arrival lines
+    add(p.off_long_state, p.off_cand);     // tile select: state, histograms
+    add(p.off_st_ticket, p.off_st_partial);  // ticket line, control lines
+    add(p.off_op_partial, p.ws_bytes);     // tagged stats and shifts
+    return n;
+}
+
+std::mutex g_ws_mu;
+std::unordered_map<uint64_t, uint64_t> g_ws_layout;  // (device, workspace address) -> ranges' hash
+
+int prepare_ws(const Plan &p, char *ws, hipStream_t stream) {
+    CtlRange r[kMaxClearRanges];
+    const int n = control_ranges(p, r);
+    uint64_t h = 1469598103934665603ull;  // FNV-1a over the ranges
+    auto mix = [&](uint64_t v) {
+        for (int b = 0; b < 8; ++b) h = (h ^ ((v >> (8 * b)) & 0xFF)) * 1099511628211ull;
+    };
+    for (int i = 0; i < n; ++i) {
+        mix(r[i].off);
+        mix(r[i].bytes);
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(SNAPKV_EHIP, "hipGetDevice failed");
+    const uint64_t key = (uint64_t)(uintptr_t)ws ^ ((uint64_t)dev << 56);
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_layout.find(key);
+    if (it != g_ws_layout.end() && it->second == h) return SNAPKV_OK;
+    if (n > 0) {
+        WsClearParams cp;
+        memset(&cp, 0, sizeof cp);
+        cp.base = (unsigned char *)ws;
+        int64_t most = 0;
+        for (int i = 0; i < n; ++i) {
+            cp.off[i] = (int64_t)r[i].off;
+            cp.n16[i] = (int64_t)(r[i].bytes / 16);
+            most = cp.n16[i] > most ? cp.n16[i] : most;
+        }
+        cp.n_ranges = n;
+        int64_t blocks = (most + 255) / 256;
+        blocks = blocks > 1024 ? 1024 : (blocks < 1 ? 1 : blocks);
+        const int st = launch(SNAPKV_K_WS_CLEAR, ws_clear(), dim3((unsigned)blocks), dim3(256), &cp, stream);
+        if (st) return st;
+    }
+    g_ws_layout[key] = h;
+    return SNAPKV_OK;
+}
+
 int check_ptr(const void *ptr, const char *name) {
     if (!ptr) return fail(SNAPKV_EINVAL, std::string(name) + " is NULL");
     if (!aligned16(ptr)) return fail(SNAPKV_EINVAL, std::string(name) + " must be 16-byte aligned");
@@ -872,6 +935,7 @@ static int scores_impl(const snapkv_problem *pb, const void *q_obs, const void *
     if (!st) st = check_opt_ptr(votes, "votes");
     if (!st) st = check_ptr(pooled, "pooled");
     if (!st) st = check_ws(p, ws, ws_bytes);
+    if (!st) st = prepare_ws(p, (char *)ws, (hipStream_t)stream);
     if (st) return st;
     char *w = (char *)ws;
     float *v = votes ? votes : (float *)(w + p.off_votes);
@@ -895,6 +959,7 @@ int snapkv_select(const snapkv_problem *pb, const float *pooled, int32_t *idx, v
     if (!st) st = check_ptr(pooled, "pooled");
     if (!st) st = check_ptr(idx, "idx");
     if (!st) st = check_ws(p, ws, ws_bytes);
+    if (!st) st = prepare_ws(p, (char *)ws, (hipStream_t)stream);
     if (st) return st;
     DevInfo di;
     st = device_info(&di);
@@ -943,6 +1008,8 @@ static int compress_impl(const snapkv_problem *pb, const void *q_obs, const void
         st = scratch_for_device(s, &ws);
         if (st) return st;
     }
+    st = prepare_ws(p, (char *)ws, s);
+    if (st) return st;
     char *w = (char *)ws;
     float *votes = (float *)(w + p.off_votes);
     // pooled votes: the caller's buffer, or workspace when long segments need them in memory
@@ -1175,6 +1242,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_DECODE_COMBINE: return "decode_combine";
         case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
         case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
+        case SNAPKV_K_WS_CLEAR: return "ws_clear";
         case SNAPKV_K_OBS_STREAM: return "obs_score_stream";
         case SNAPKV_K_OBS_ONEPASS: return "obs_score_onepass";
         case SNAPKV_K_OBS_ONEPASS2: return "obs_score_onepass2";

@@ -612,6 +612,17 @@ __global__ void __launch_bounds__(256) hit_clear_kernel(const ClearParams p) {
     if (i < p.n) p.data[i] = 0u;
 }
 
+// Workspace ranges a call expects to find at zero (see the host's control_ranges), 16-byte
+// stores over a grid-stride loop.
+__global__ void __launch_bounds__(256) ws_clear_kernel(const WsClearParams p) {
+    for (int r = 0; r < p.n_ranges; ++r) {
+        u32x4_t *const d = (u32x4_t *)(p.base + p.off[r]);
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < p.n16[r]; i += (int64_t)gridDim.x * 256)
+            d[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+const void *ws_clear() { return (const void *)&ws_clear_kernel; }
+
 __global__ void __launch_bounds__(kSelThreads) hit_rate_kernel(const HitParams p) {
     __shared__ uint32_t bits[kHitTile / 32];
     __shared__ int range[2];

@@ -203,6 +203,14 @@ struct ClearParams {
     int32_t n;
 };
 const void *hit_clear();       // zeroes data[0, n); grid ceil(n / 256) x 256 threads (also used to clear scratch)
+constexpr int kMaxClearRanges = 4;
+struct WsClearParams {
+    unsigned char *base;
+    int64_t off[kMaxClearRanges];  // byte offsets (16-byte aligned)
+    int64_t n16[kMaxClearRanges];  // lengths in 16-byte units
+    int32_t n_ranges;
+};
+const void *ws_clear();        // zeroes the ranges; any grid of 256-thread workgroups
 int hit_tile_positions();      // positions per hit_rate workgroup (grid x = tiles of the longest)
 
 struct DecodeParams {

@@ -257,6 +257,10 @@ ONEPASS2 = [
     ("onepass2_gqa_M32", [70000, 3000], 16, 8, 128, "bf16", 16, 7, 0.05, None, 16, 0),
     ("onepass2_f32_d64", [40000, 30000], 8, 8, 64, "f32", 32, 5, None, 1000, 16, 0),
     ("onepass2_prefix_only", [70000, 1500, 32], 8, 8, 128, "bf16", 32, 7, 0.05, None, 16, 1),
+    # 64 requests in two groups of 32: ~12 items per workgroup from segments of 1 to 39 items,
+    # per-item and central merging interleaved in every workgroup
+    ("onepass2_many_segments", [700 + (i * 7919) % 39000 for i in range(64)], 8, 8, 128, "bf16", 32, 7, 0.05, None,
+     4, 0),
 ]
 
 
@@ -621,6 +625,44 @@ def test_workspace_reuse_across_inputs(case):
             check_scores(pooled[g, cols], rr["pooled"], tag + " pooled")
             check_selection(idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])], rr["pooled"], rr["idx"], rr["k"],
                             tag + " select")
+
+
+# One workspace across problems of different shapes: each call's counters and tagged slots
+# lie where the previous call may have written votes or indices, so a call on a workspace last
+# used with another layout clears its own control regions first.  Every call must give the
+# same bits as the same call on a fresh zero-filled workspace.
+RESHAPE = [
+    # lengths, Hq, Hkv, flags: two-slot one-read (tile select past 32768 positions), two-phase
+    # stream (GQA), one-read, fused (forced), then the first again
+    ([300000, 40000], 2, 2, {}),
+    ([20000, 7000], 16, 4, {}),
+    ([9000, 3000], 4, 4, {}),
+    ([3000, 1800], 8, 2, {"fused": True}),
+    ([300000, 40000], 2, 2, {}),
+]
+
+
+def test_workspace_reuse_across_shapes():
+    snap = _snap()
+    cases = []
+    for n, (lengths, Hq, Hkv, flags) in enumerate(RESHAPE):
+        wl = synth.custom(lengths, Hq, Hkv, 128, obs_window=32, pool_kernel=7, ratio=0.05, n_plant=8,
+                          name="reshape%d" % n)
+        x = synth.make_inputs(wl, n % 2, threads=16)
+        q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+        spec = snap.make_spec(q, K, x["cu_seqlens"], 32, 7, 0.05, None, **flags)
+        cases.append((q, K, V, x["cu_seqlens"], flags, spec.ws_bytes))
+    shared = torch.zeros(max(c[5] for c in cases), dtype=torch.uint8, device="cuda")
+    kw = dict(obs_window=32, pool_kernel=7, ratio=0.05, want_pooled=True)
+    for n, (q, K, V, cu, flags, nbytes) in enumerate(cases):
+        _say("reshape call %d %s" % (n, RESHAPE[n][:3]))
+        fresh = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        ref = snap.compress(q, K, V, cu, ws=fresh, **kw, **flags)
+        got = snap.compress(q, K, V, cu, ws=shared[:nbytes], **kw, **flags)
+        torch.cuda.synchronize()
+        for key in ("pooled", "idx", "K_out", "V_out"):
+            assert torch.equal(got[key], ref[key]), "call %d: %s differs from a fresh workspace's" % (n, key)
+        assert int(shared[:4].view(torch.int32).item()) == 0
 
 
 def test_workspace_counters_left_zero():

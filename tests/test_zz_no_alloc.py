@@ -17,8 +17,10 @@ def _snap():
 
 
 CASES = [
-    # lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant  (second call smaller)
-    ([5000, 9000, 3000], 16, 4, 128, "bf16", 32, 7, 0.05, None, 16),
+    # lengths, Hq, Hkv, d, dtype, w, K_pool, ratio, budget, n_plant  (each call smaller than the last)
+    ([70000, 1500], 8, 8, 128, "bf16", 32, 7, 0.05, None, 8),    # two-slot one-read scoring
+    ([5000, 9000, 3000], 16, 4, 128, "bf16", 32, 7, 0.05, None, 16),  # two-phase streaming scoring
+    ([9000, 3000], 4, 4, 128, "bf16", 32, 7, 0.05, None, 8),     # one-read scoring
     ([1500], 8, 2, 128, "bf16", 32, 7, None, 100, 8),
 ]
 
