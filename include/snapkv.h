@@ -290,7 +290,7 @@ typedef enum {
     SNAPKV_K_SELECT = 6,      /* topk_select */
     SNAPKV_K_GATHER = 7,      /* kv_gather */
     SNAPKV_K_SUM_CHUNKS = 8,  /* sum of the votes of the row chunks (G * L_obs > 32) */
-    SNAPKV_K_SELECT_TILES = 9, /* topk_select of segments longer than 32768 positions (4 phases) */
+    SNAPKV_K_SELECT_TILES = 9, /* topk_select of segments longer than 32768 positions (3 launches) */
     SNAPKV_K_HIT_RATE = 10,    /* snapkv_hit_rate */
     SNAPKV_K_DECODE = 11,      /* snapkv_decode: split-K partials */
     SNAPKV_K_DECODE_COMBINE = 12, /* snapkv_decode: merge of the splits */

@@ -747,7 +747,7 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
             lp.max_tiles = p.max_tiles;
             lp.rt = gr.rt;
             const int tiles = (gr.max_P + select_tile_positions() - 1) / select_tile_positions();
-            for (int phase = 0; phase < 4; ++phase) {
+            for (int phase : {0, 1, 3}) {  // phase 1's last tile records what a phase 2 would
                 lp.phase = phase;
                 int st = launch(SNAPKV_K_SELECT_TILES, long_kernel(), dim3(tiles, gr.rt.n * p.Hkv),
                                 dim3(select_threads()), &lp, stream);

@@ -298,14 +298,16 @@ __device__ __forceinline__ void select_resident(const SelectParams &p, uint32_t 
 }
 
 // ---- segments longer than kSelLds -----------------------------------------------------------
-// Tiles of kTile positions, one workgroup each, in four launches (phase 0..3):
+// Tiles of kTile positions, one workgroup each, in three launches (phases 0, 1, 3):
 //   0: pool the tile (halo from the neighbours' votes), write the pooled votes, add a
 //      4096-bin histogram of bits 30..19 to the segment's global histogram; the tile that
 //      finishes last picks the bin b of the k-th value and clears the histogram.
 //   1: each tile counts its values above bin b, records that count, and appends its values
 //      in bin b to the segment's candidate list (recording where); the last tile refines
-//      the exact k-th value among the candidates (bits 18..8, then 7..0).
-//   2: each tile's counts above / equal to that value, from its record and its candidates.
+//      the exact k-th value among the candidates (bits 18..8, then 7..0) and then records
+//      every tile's counts above / equal to that value (one wave per tile, over the tile's
+//      candidates).  When the whole bin b is taken there is nothing to refine and each tile
+//      records its own counts.
 //   3: each tile adds the counts of the tiles before it and writes its positions in order.
 // "Last" is decided by a per-segment arrival counter that the last tile resets, so no
 // workgroup ever waits for another.  Full passes over the tile use coalesced loads (LDS
@@ -454,9 +456,13 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         if (tid == 0) {
             const uint32_t o0 = refine ? __hip_atomic_fetch_add(&st->ncand, ctot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
             s.sh[3] = o0;
-            rec[0] = gtot;
-            rec[1] = o0;
-            rec[2] = ctot;
+            // agent-scope stores: the segment's last tile reads them in this launch
+            __hip_atomic_store(&rec[0], gtot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rec[1], o0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rec[2], ctot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the whole bin is taken: every value in it counts as equal (counts fit 16 bits:
+            // a tile holds at most kTile positions)
+            if (!refine) rec[3] = (gtot & 0xFFFFu) | (ctot << 16);
         }
         if (!refine) return;
         __syncthreads();
@@ -500,33 +506,29 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
             st->mask = pv.mask;
             st->need = pv.need;
         }
+        // every tile's counts above / equal to the pivot: its values above bin b (its record)
+        // plus its candidates above the pivot, and its candidates equal to it
+        const uint32_t *recs = p.tilecnt + (int64_t)seg * p.max_tiles * 4;
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int t = wave; t < (int)n_tiles; t += kSelWaves) {
+            uint32_t *rt = (uint32_t *)recs + 4 * t;
+            const uint32_t above0 = __hip_atomic_load(&rt[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t o0 = __hip_atomic_load(&rt[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t nc = __hip_atomic_load(&rt[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t i = lane; i < nc; i += 64) {
+                const uint32_t m = __hip_atomic_load(&cand[o0 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & pv.mask;
+                gt += m > pv.prefix ? 1u : 0u;
+                eq += m == pv.prefix ? 1u : 0u;
+            }
+            gt = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(gt), 63);
+            eq = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(eq), 63);
+            if (lane == 0) rt[3] = ((above0 + gt) & 0xFFFFu) | (eq << 16);
+        }
         return;
     }
 
     const uint32_t prefix = st->prefix, mask = st->mask, need = st->need;
-    if (p.phase == 2) {
-        // counts above / equal to the pivot: the values above the first bin, plus this
-        // tile's candidates (all of them when the first bin was taken whole)
-        uint32_t gt = 0, eq = 0;
-        const uint32_t o0 = rec[1], nc = rec[2];
-        if (st->done) {
-            eq = tid == 0 ? nc : 0u;
-        } else {
-            const uint32_t *cand = p.cand + base;
-            for (uint32_t i = tid; i < nc; i += kSelThreads) {
-                const uint32_t m = cand[o0 + i] & mask;
-                gt += m > prefix ? 1u : 0u;
-                eq += m == prefix ? 1u : 0u;
-            }
-        }
-        uint32_t gtot, etot;
-        (void)block_excl_scan_t(gt, &gtot, s.wtot);
-        __syncthreads();
-        (void)block_excl_scan_t(eq, &etot, s.wtot);
-        if (tid == 0) rec[3] = ((rec[0] + gtot) & 0xFFFFu) | (etot << 16);
-        return;
-    }
-
     // phase 3: ordered writes after the counts of the tiles before this one
     {
         uint32_t t[16];
