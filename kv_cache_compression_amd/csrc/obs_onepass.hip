@@ -397,7 +397,9 @@ obs_onepass_kernel(const StreamParams p) {
                 static_for<RTW>([&](auto rt) { static_for<4>([&](auto i) { v = fmaf(E[s][rt][i], f[rt][i], v); }); });
                 v = cross_row_sum4(v);
                 const int j = key0 + s * kStepKeys + wave * 16 + n16;
-                if (grp == 0 && j < vis_end) vout[j] = v;
+                // non-temporal: the votes are read once, by the next launch (0.5 us less per
+                // step at the 16K-token layer)
+                if (grp == 0 && j < vis_end) __builtin_nontemporal_store(v, &vout[j]);
             });
         }
 
