@@ -463,7 +463,9 @@ obs_onepass2_kernel(const StreamParams p) {
                 static_for<RTW>([&](auto rt) { static_for<4>([&](auto i) { v = fmaf(E[SL][s][rt][i], f[rt][i], v); }); });
                 v = cross_row_sum4(v);
                 const int j = it.key0 + s * kStepKeys + wave * 16 + n16;
-                if (grp == 0 && j < vis_end) vout[j] = v;
+                // non-temporal: the votes are read once, by the next launch (5 us less at the
+                // 380K-token layer)
+                if (grp == 0 && j < vis_end) __builtin_nontemporal_store(v, &vout[j]);
             });
         }
         lds_barrier();  // sh_flag, sh_fin and sh_lsh of this slot are free again
