@@ -316,9 +316,9 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     const bool op_ok = p.st_ok && p.st_rows == 32;
     int64_t op_max_items = 0;  // items of the largest group at the one-read kernels' smallest slab
     if (op_ok) {
-        int thr = 0, slab1 = 0, slab2 = 0;
+        int thr = 0, slab1 = 0, slab2 = 0, slots = 0;
         (void)onepass_kernel(p.dtype, &thr, &slab1);
-        (void)onepass2_kernel(p.dtype, &thr, &slab2);
+        (void)onepass2_kernel(p.dtype, &thr, &slab2, &slots);
         const int slab = slab1 < slab2 ? slab1 : slab2;
         for (const Group &gr : p.groups) {
             const int64_t n = stream_items(p, gr, slab, nullptr);
@@ -466,8 +466,8 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
     int op_threads = 0, op_slab = 0;
     const void *ko = p.st_ok && p.st_rows == 32 ? onepass_kernel(p.dtype, &op_threads, &op_slab) : nullptr;
     const int op_grid = ko ? occupancy(ko, op_threads) * di.cus : 0;
-    int o2_threads = 0, o2_slab = 0;
-    const void *ko2 = ko ? onepass2_kernel(p.dtype, &o2_threads, &o2_slab) : nullptr;
+    int o2_threads = 0, o2_slab = 0, o2_slots = 0;
+    const void *ko2 = ko ? onepass2_kernel(p.dtype, &o2_threads, &o2_slab, &o2_slots) : nullptr;
     const int o2_grid = ko2 ? occupancy(ko2, o2_threads) * di.cus : 0;
     const bool forced = (p.flags & (SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED)) != 0;
     for (const Group &gr : p.groups) {
@@ -488,7 +488,7 @@ int run_scores(const Plan &p, const void *q, const void *K, const float *lse, fl
         const bool use_onepass = ko && !lse && !forced && op_grid > 0 && op_items <= op_grid && op_max_ns <= op_grid;
         const int o2_launch = o2_items < o2_grid ? (int)o2_items : o2_grid;
         const bool use_onepass2 = !use_onepass && ko2 && !lse && !forced && o2_launch > 0 &&
-                                  o2_max_ns <= 2 * o2_launch;
+                                  o2_max_ns <= o2_slots * o2_launch;
         const bool use_stream = !use_onepass && !use_onepass2 && p.st_ok && st_grid > 0 && !(p.flags & SNAPKV_FLAG_FUSED) &&
                                 !(p.flags & SNAPKV_FLAG_TWO_PASS);
         const bool one_read = use_onepass || use_onepass2;

@@ -66,8 +66,9 @@ struct Item2 {
 
 }  // namespace
 
-// NW waves per workgroup, RES steps (16 * NW keys each) per slot, DEPTH steps of keys in flight.
-template <typename T, int NW, int RES, int DEPTH>
+// NW waves per workgroup, RES steps (16 * NW keys each) per slot, DEPTH steps of keys in flight,
+// NS slots (items held at once).
+template <typename T, int NW, int RES, int DEPTH, int NS>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 obs_onepass2_kernel(const StreamParams p) {
     constexpr int NT = 64 * NW;
@@ -84,8 +85,8 @@ obs_onepass2_kernel(const StreamParams p) {
 
     __shared__ u32x4_t sh_k[NW][256];        // each wave's staging tile (no other wave touches it)
     __shared__ float sh_ms[NW][MROWS], sh_ml[NW][MROWS];
-    __shared__ float sh_lsh[2][NW][MROWS];   // per slot: each wave's row shifts (-inf: no weights)
-    __shared__ float sh_fin[2][MROWS];       // per slot: segment row shifts, +inf for padding rows
+    __shared__ float sh_lsh[NS][NW][MROWS];  // per slot: each wave's row shifts (-inf: no weights)
+    __shared__ float sh_fin[NS][MROWS];      // per slot: segment row shifts, +inf for padding rows
     __shared__ u32x4_t sh_q[MROWS * 16];     // the next item's query rows (slot 16 row + (chunk ^ row % 16))
     __shared__ int sh_wrow[MROWS];
     __shared__ int sh_flag;
@@ -123,7 +124,7 @@ obs_onepass2_kernel(const StreamParams p) {
     };
     auto ctl = [&](int seg, int line) { return p.seg_ctl + (int64_t)seg * 3 * kStreamSegLine + line * kStreamSegLine; };
     auto fin_slot = [&](int seg) { return (uint32_t *)p.final_shift + (int64_t)seg * MROWS; };
-    float E[2][RES][RTW][4];
+    float E[NS][RES][RTW][4];
     u32x4_t kreg[DEPTH][4];  // key rows in flight (the first DEPTH steps of an item can be prefetched)
     const int row4 = 4 * (int)tstride;
 
@@ -471,27 +472,30 @@ obs_onepass2_kernel(const StreamParams p) {
         lds_barrier();  // sh_flag, sh_fin and sh_lsh of this slot are free again
     };
 
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
     // Items are dealt round robin: workgroup w takes items w, w + G, w + 2G, ... (G workgroups,
-    // at most N), slot 0 and slot 1 in turn.  Each item's queries and first keys are issued
-    // before the workgroup finishes its older item.
+    // at most N); its item number i goes to slot i % NS.  After scoring item i the workgroup
+    // finishes item i - (NS - 1), whose slot is the next to fill; each item's queries and first
+    // keys are issued before that finish.
     const int G = (int)gridDim.x;
-    int ia = (int)blockIdx.x, ib = ia + G;
-    issue_first(ia);
-    stream_item(S0{}, ia);
-    if (ib < N) issue_first(ib);
-    for (;;) {
-        if (ib < N) stream_item(S1{}, ib);
-        if (ib < N && ia + 2 * G < N) issue_first(ia + 2 * G);
-        finish_item(S0{}, ia);
-        if (ib >= N) break;
-        ia += 2 * G;
-        if (ia < N) stream_item(S0{}, ia);
-        if (ia < N && ib + 2 * G < N) issue_first(ib + 2 * G);
-        finish_item(S1{}, ib);
-        if (ia >= N) break;
-        ib += 2 * G;
+    const int w0 = (int)blockIdx.x;
+    issue_first(w0);
+    for (int base = w0;; base += NS * G) {
+        bool done = false;
+        static_for<NS>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            if (done) return;
+            const int item = base + S * G;        // scored at this step, into slot S
+            const int fin = item - (NS - 1) * G;  // finished at this step, from slot (S + 1) % NS
+            if (item < N) {
+                stream_item(std::integral_constant<int, S>{}, item);
+                if (item + G < N) issue_first(item + G);
+            }
+            if (fin >= w0) {
+                finish_item(std::integral_constant<int, (S + 1) % NS>{}, fin);
+                done = fin + G >= N;  // that was the workgroup's last item
+            }
+        });
+        if (done) break;
     }
     // the last finish's reader count
     if ((int)threadIdx.x == 0) sh_flag = pending_clear_flag() ? 1 : 0;
@@ -501,13 +505,14 @@ obs_onepass2_kernel(const StreamParams p) {
 
 // Eight waves per workgroup (one workgroup per CU), two slots of 1024 keys.
 template <typename T>
-static const void *onepass2_pick(int *threads, int *slab) {
+static const void *onepass2_pick(int *threads, int *slab, int *slots) {
     *threads = 64 * 8;
     *slab = 16 * 8 * 8;
-    return (const void *)&obs_onepass2_kernel<T, 8, 8, 2>;
+    *slots = 2;
+    return (const void *)&obs_onepass2_kernel<T, 8, 8, 2, 2>;
 }
-const void *onepass2_kernel(int dtype, int *threads, int *slab) {
-    return dtype == 1 ? onepass2_pick<__bf16>(threads, slab) : onepass2_pick<float>(threads, slab);
+const void *onepass2_kernel(int dtype, int *threads, int *slab, int *slots) {
+    return dtype == 1 ? onepass2_pick<__bf16>(threads, slab, slots) : onepass2_pick<float>(threads, slab, slots);
 }
 
 }  // namespace snapkv

@@ -122,7 +122,9 @@ const void *stream_kernel(int dtype, int rows, int *threads);
 // one-read streaming kernel for up to 32 rows per KV head, keys of 256 bytes; *threads = its
 // workgroup size, *slab = the keys of one item
 const void *onepass_kernel(int dtype, int *threads, int *slab);
-const void *onepass2_kernel(int dtype, int *threads, int *slab);
+// the same with several items in flight per workgroup; *slots = items held at once (a segment
+// may have up to slots x grid items)
+const void *onepass2_kernel(int dtype, int *threads, int *slab, int *slots);
 
 struct MergeParams {
     const float2 *partial;
