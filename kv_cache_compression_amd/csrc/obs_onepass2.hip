@@ -81,7 +81,8 @@ obs_onepass2_kernel(const StreamParams p) {
     constexpr int TPR = NT / MROWS;  // threads per row in the central merge
     static_assert(TPR >= 1 && (TPR & (TPR - 1)) == 0, "threads per row");
     static_assert(MROWS == 32, "a wave polls two items per row per load round");
-    static_assert(NT == MROWS * 16, "one 16-byte query chunk per thread");
+    static_assert((MROWS * 16) % NT == 0, "whole 16-byte query chunks per thread");
+    constexpr int QCH = MROWS * 16 / NT;  // query chunks each thread copies
 
     __shared__ u32x4_t sh_k[NW][256];        // each wave's staging tile (no other wave touches it)
     __shared__ float sh_ms[NW][MROWS], sh_ml[NW][MROWS];
@@ -100,7 +101,7 @@ obs_onepass2_kernel(const StreamParams p) {
     uint64_t *const slots = (uint64_t *)p.partial;  // [item][32]: (shift, sum | kSumTag), 0 = unwritten
 
     for (int r = tid; r < MROWS; r += NT) sh_wrow[r] = r % p.w;
-    sh_q[tid] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = tid; i < MROWS * 16; i += NT) sh_q[i] = u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
 
     auto decode = [&](int item) {
@@ -146,11 +147,13 @@ obs_onepass2_kernel(const StreamParams p) {
             const char *qb = (const char *)p.q + (((int64_t)p.rt.qi[it.r] * p.Hq + (int64_t)it.g * p.G) * (int64_t)p.w) * ROWB;
             const __amdgpu_buffer_rsrc_t qrsrc =
                 __builtin_amdgcn_make_buffer_rsrc((void *)qb, (short)0, p.M * ROWB, kBufferFlags);
-            const int slot = tl & (NT - 1);
-            const int qrow = slot >> 4, qch = (slot & 15) ^ (qrow & 15);
-            const int vw = __builtin_amdgcn_readfirstlane(tl >> 6);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void *)&sh_q[64 * vw], 16,
-                                                     qrow * ROWB + qch * 16, 0, 0, 0);
+            static_for<QCH>([&](auto cc) {
+                const int slot = cc() * NT + (tl & (NT - 1));
+                const int qrow = slot >> 4, qch = (slot & 15) ^ (qrow & 15);
+                const int vw = __builtin_amdgcn_readfirstlane(cc() * NW + (tl >> 6));
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(qrsrc, (__attribute__((address_space(3))) void *)&sh_q[64 * vw],
+                                                         16, qrow * ROWB + qch * 16, 0, 0, 0);
+            });
         }
         asm volatile("" ::: "memory");  // the copy is issued before the key loads
         const __amdgpu_buffer_rsrc_t rsrc = item_rsrc(it);
