@@ -750,7 +750,7 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
             for (int phase : {0, 1, 3}) {  // phase 1's last tile records what a phase 2 would
                 lp.phase = phase;
                 int st = launch(SNAPKV_K_SELECT_TILES, long_kernel(), dim3(tiles, gr.rt.n * p.Hkv),
-                                dim3(select_threads()), &lp, stream);
+                                dim3(long_threads()), &lp, stream);
                 if (st) return st;
             }
         }

@@ -112,14 +112,15 @@ struct SelectShared {
     uint32_t wand[kSelWaves], wor[kSelWaves];
 };
 
-// Exclusive prefix sum of x over the workgroup (one barrier); *total gets the sum.
+// Exclusive prefix sum of x over a workgroup of NWAVES waves (one barrier); *total gets the sum.
+template <int NWAVES = kSelWaves>
 __device__ __forceinline__ uint32_t block_excl_scan_t(uint32_t x, uint32_t *total, uint32_t *wtot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(x);
     if (lane == 63) wtot[wave] = incl;
     __syncthreads();
     uint32_t woff = 0, tot = 0;
-    static_for<kSelWaves>([&](auto w2) {
+    static_for<NWAVES>([&](auto w2) {
         const uint32_t t = wtot[w2()];
         woff += w2() < wave ? t : 0u;
         tot += t;
@@ -312,14 +313,17 @@ __device__ __forceinline__ void select_resident(const SelectParams &p, uint32_t 
 // "Last" is decided by a per-segment arrival counter that the last tile resets, so no
 // workgroup ever waits for another.  Full passes over the tile use coalesced loads (LDS
 // holds the tile where a thread needs its own contiguous run).
-constexpr int kTile = 16 * kSelThreads;
+constexpr int kLongThreads = 512;  // two tiles per CU (registers), so a launch runs 512 tiles at once
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kTile = 16 * kLongThreads;
 constexpr int kLongBins = 4096;
 int select_tile_positions() { return kTile; }
+int long_threads() { return kLongThreads; }
 
 struct LongShared {
     uint32_t hist[kLongBins];
     uint32_t sh[4];
-    uint32_t wtot[kSelWaves];
+    uint32_t wtot[kLongWaves];
     uint32_t last;
 };
 
@@ -338,15 +342,15 @@ __device__ __forceinline__ bool arrive_last(uint32_t *counter, uint32_t n_tiles,
     return s.last != 0;
 }
 
-// Coalesced load of the tile's values: position start + i * kSelThreads + tid at u[i].
+// Coalesced load of the tile's values: position start + i * kLongThreads + tid at u[i].
 __device__ __forceinline__ void load_tile_strided(const uint32_t *src, int P, int start, uint32_t (&u)[16]) {
     static_for<16>([&](auto i) {
-        const int j = start + i() * kSelThreads + (int)threadIdx.x;
+        const int j = start + i() * kLongThreads + (int)threadIdx.x;
         u[i()] = j < P ? src[j] : 0u;
     });
 }
 
-__global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams p) {
+__global__ void __launch_bounds__(kLongThreads) topk_long_kernel(const LongParams p) {
     constexpr int HA = kSelMaxHalfAll;
     __shared__ __attribute__((aligned(16))) uint32_t sdata[kTile + 2 * HA];
     __shared__ __attribute__((aligned(16))) LongShared s;
@@ -377,8 +381,8 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
             h0 = jl >= 0 ? src[jl] : 0u;
             h1 = jr < P ? src[jr] : 0u;
         }
-        for (int i = tid; i < kLongBins; i += kSelThreads) s.hist[i] = 0;
-        static_for<16>([&](auto i) { sdata[i() * kSelThreads + tid + HA] = t[i()]; });
+        for (int i = tid; i < kLongBins; i += kLongThreads) s.hist[i] = 0;
+        static_for<16>([&](auto i) { sdata[i() * kLongThreads + tid + HA] = t[i()]; });
         if (tid < HA) {
             sdata[tid] = h0;
             sdata[kTile + HA + tid] = h1;
@@ -395,8 +399,8 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
             __syncthreads();
             uint32_t *dst = (uint32_t *)(p.pooled + base);
             static_for<16>([&](auto i) {
-                const int j = start + i() * kSelThreads + tid;
-                if (j < P) dst[j] = sdata[i() * kSelThreads + tid + HA];
+                const int j = start + i() * kLongThreads + tid;
+                if (j < P) dst[j] = sdata[i() * kLongThreads + tid + HA];
             });
         } else {
             static_for<16>([&](auto i) { u[i()] = sdata[16 * tid + i() + HA]; });
@@ -413,11 +417,11 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         });
         __syncthreads();
         uint32_t *gh = p.ghist + (int64_t)seg * kLongBins;
-        for (int i = tid; i < kLongBins; i += kSelThreads)
+        for (int i = tid; i < kLongBins; i += kLongThreads)
             if (s.hist[i]) __hip_atomic_fetch_add(&gh[i], s.hist[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (!arrive_last(&st->arrived, n_tiles, s)) return;
         // last tile: the segment's histogram -> LDS (and cleared for the next call)
-        for (int i = tid; i < kLongBins; i += kSelThreads) {
+        for (int i = tid; i < kLongBins; i += kLongThreads) {
             s.hist[i] = __hip_atomic_load(&gh[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&gh[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -444,15 +448,15 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         load_tile_strided(src, P, start, u);
         uint32_t gt = 0, c = 0;
         static_for<16>([&](auto i) {
-            const int j = start + i() * kSelThreads + tid;
+            const int j = start + i() * kLongThreads + tid;
             const uint32_t m = u[i()] & 0x7FFFFFFFu & mask;
             gt += (j < P && m > prefix) ? 1u : 0u;
             c += (j < P && m == prefix) ? 1u : 0u;
         });
         uint32_t gtot, ctot;
-        (void)block_excl_scan_t(gt, &gtot, s.wtot);
+        (void)block_excl_scan_t<kLongWaves>(gt, &gtot, s.wtot);
         __syncthreads();
-        const uint32_t cexcl = block_excl_scan_t(c, &ctot, s.wtot);
+        const uint32_t cexcl = block_excl_scan_t<kLongWaves>(c, &ctot, s.wtot);
         if (tid == 0) {
             const uint32_t o0 = refine ? __hip_atomic_fetch_add(&st->ncand, ctot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
             s.sh[3] = o0;
@@ -469,7 +473,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         uint32_t *cand = p.cand + base;
         uint32_t o = s.sh[3] + cexcl;
         static_for<16>([&](auto i) {
-            const int j = start + i() * kSelThreads + tid;
+            const int j = start + i() * kLongThreads + tid;
             const uint32_t v = u[i()] & 0x7FFFFFFFu;
             if (j < P && (v & mask) == prefix) __hip_atomic_store(&cand[o++], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         });
@@ -480,16 +484,16 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         static_for<2>([&](auto pass) {
             constexpr int shift = decltype(pass)::value == 0 ? 8 : 0;
             constexpr uint32_t dmask = decltype(pass)::value == 0 ? 0x7FFu : 0xFFu;
-            for (int i = tid; i < kLongBins; i += kSelThreads) s.hist[i] = 0;
+            for (int i = tid; i < kLongBins; i += kLongThreads) s.hist[i] = 0;
             __syncthreads();
-            for (int i0 = tid; i0 < ncand; i0 += 8 * kSelThreads) {  // eight loads in flight
+            for (int i0 = tid; i0 < ncand; i0 += 8 * kLongThreads) {  // eight loads in flight
                 uint32_t v[8];
                 static_for<8>([&](auto e) {
-                    const int i = i0 + e() * kSelThreads;
+                    const int i = i0 + e() * kLongThreads;
                     v[e()] = i < ncand ? __hip_atomic_load(&cand[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
                 });
                 static_for<8>([&](auto e) {
-                    if (i0 + e() * kSelThreads < ncand && (v[e()] & pv.mask) == pv.prefix)
+                    if (i0 + e() * kLongThreads < ncand && (v[e()] & pv.mask) == pv.prefix)
                         atomicAdd(&s.hist[(v[e()] >> shift) & dmask], 1u);
                 });
             }
@@ -510,7 +514,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         // plus its candidates above the pivot, and its candidates equal to it
         const uint32_t *recs = p.tilecnt + (int64_t)seg * p.max_tiles * 4;
         const int lane = tid & 63, wave = tid >> 6;
-        for (int t = wave; t < (int)n_tiles; t += kSelWaves) {
+        for (int t = wave; t < (int)n_tiles; t += kLongWaves) {
             uint32_t *rt = (uint32_t *)recs + 4 * t;
             const uint32_t above0 = __hip_atomic_load(&rt[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t o0 = __hip_atomic_load(&rt[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -533,19 +537,19 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
     {
         uint32_t t[16];
         load_tile_strided(src, P, start, t);
-        static_for<16>([&](auto i) { sdata[i() * kSelThreads + tid] = t[i()]; });
+        static_for<16>([&](auto i) { sdata[i() * kLongThreads + tid] = t[i()]; });
     }
     uint32_t pgt = 0, peq = 0;
     const uint32_t *recs = p.tilecnt + (int64_t)seg * p.max_tiles * 4;
-    for (int t = tid; t < (int)blockIdx.x; t += kSelThreads) {
+    for (int t = tid; t < (int)blockIdx.x; t += kLongThreads) {
         const uint32_t v = recs[4 * t + 3];
         pgt += v & 0xFFFFu;
         peq += v >> 16;
     }
     uint32_t gt_base, eq_base;
-    (void)block_excl_scan_t(pgt, &gt_base, s.wtot);
+    (void)block_excl_scan_t<kLongWaves>(pgt, &gt_base, s.wtot);
     __syncthreads();
-    (void)block_excl_scan_t(peq, &eq_base, s.wtot);  // its barrier also publishes sdata
+    (void)block_excl_scan_t<kLongWaves>(peq, &eq_base, s.wtot);  // its barrier also publishes sdata
     __syncthreads();
     uint32_t u[16];
     static_for<16>([&](auto i) { u[i()] = sdata[16 * tid + i()] & 0x7FFFFFFFu; });
@@ -555,7 +559,7 @@ __global__ void __launch_bounds__(kSelThreads) topk_long_kernel(const LongParams
         if (i() < nvalid) packed += m > prefix ? 1u : (m == prefix ? 0x10000u : 0u);
     });
     uint32_t total;
-    const uint32_t excl = block_excl_scan_t(packed, &total, s.wtot);
+    const uint32_t excl = block_excl_scan_t<kLongWaves>(packed, &total, s.wtot);
     uint32_t gt_before = gt_base + (excl & 0xFFFFu), eq_before = eq_base + (excl >> 16);
     static_for<16>([&](auto i) {
         const uint32_t m = u[i()] & mask;

@@ -189,6 +189,7 @@ struct LongParams {
 };
 const void *long_kernel();
 int select_tile_positions();
+int long_threads();             // workgroup size of long_kernel
 
 struct HitParams {
     const float *a_cur;         // [H_kv][sum_P]
