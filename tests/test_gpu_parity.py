@@ -297,8 +297,10 @@ def test_onepass2_segment_limit(extra):
 
 
 # Segment lengths around every register-run size of the select kernel (4, 8, 16, 32
-# positions per thread of 1024) and past the 32768 positions it holds on chip.
-SELECT_P = [1, 2, 3, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 70001]
+# positions per thread of 1024), past the 32768 positions it holds on chip, and around the
+# tile kernel's 8192-position tiles (an exact multiple, a last tile of one position, one
+# position short of a tile boundary).
+SELECT_P = [1, 2, 3, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 49152, 57345, 65535, 70001]
 
 
 @pytest.mark.parametrize("levels", [0, 3, 50])
