@@ -91,6 +91,13 @@ typedef enum { SNAPKV_CAUSAL_WINDOW = 0, SNAPKV_PREFIX_ONLY = 1 } snapkv_variant
                                      problems use the two-phase kernel when it takes them, then the
                                      fused kernel, then two passes.  The three flags exclude each
                                      other. */
+#define SNAPKV_FLAG_SELECT_ONE_WG 0x8u /* top-k of segments of up to 32768 positions with one
+                                     workgroup per segment.  Without it, when a launch group has a
+                                     segment of more than 16384 positions, such segments are split
+                                     over workgroups of 8192 positions that wait for each other
+                                     (needs the launch's whole grid resident at once, which the
+                                     library checks with the occupancy API: a caller running other
+                                     kernels on the device at the same time should set it) */
 
 typedef struct {
     int32_t batch;            /* B >= 1 requests */
@@ -300,7 +307,9 @@ typedef enum {
     SNAPKV_K_OBS_ONEPASS = 16,    /* obs_score, streaming one-read kernel (<= 32 rows, weights resident) */
     SNAPKV_K_OBS_ONEPASS2 = 17,   /* obs_score, one-read kernel with two items in flight per workgroup
                                      (<= 32 rows, long segments) */
-    SNAPKV_K_WS_CLEAR = 18        /* zeroes a workspace's counters when its layout changed */
+    SNAPKV_K_WS_CLEAR = 18,       /* zeroes a workspace's counters when its layout changed */
+    SNAPKV_K_SELECT_SPLIT = 19    /* topk_select with segments of up to 32768 positions split over
+                                     workgroups of 8192 positions (all resident, two meetings) */
 } snapkv_kernel_id;
 
 int snapkv_trace_begin(void *const *events, int n_pairs);

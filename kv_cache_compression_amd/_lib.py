@@ -24,6 +24,7 @@ CAUSAL_WINDOW, PREFIX_ONLY = 0, 1
 FLAG_TWO_PASS = 0x1
 FLAG_STREAM = 0x2
 FLAG_FUSED = 0x4
+FLAG_SELECT_ONE_WG = 0x8
 
 SYMBOLS = ("snapkv_plan", "snapkv_scores", "snapkv_select", "snapkv_gather", "snapkv_compress",
            "snapkv_scores_lse", "snapkv_compress_lse", "snapkv_compress_noalloc", "snapkv_hit_rate", "snapkv_decode_plan", "snapkv_decode",
@@ -127,7 +128,7 @@ class Spec:
 
     def __init__(self, *, batch, num_q_heads, num_kv_heads, head_dim, obs_window, pool_kernel, ratio, budget,
                  dtype, cu_seqlens, kv_head_stride, kv_token_stride, variant=CAUSAL_WINDOW, two_pass=False,
-                 stream=False, fused=False):
+                 stream=False, fused=False, select_one_wg=False):
         if (ratio is None) == (budget is None):
             raise ValueError("give exactly one of ratio and budget")
         self.cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
@@ -139,7 +140,8 @@ class Spec:
         pb.mode = RATIO if ratio is not None else BUDGET
         pb.dtype = dtype
         pb.variant = variant
-        pb.flags = (FLAG_TWO_PASS if two_pass else 0) | (FLAG_STREAM if stream else 0) | (FLAG_FUSED if fused else 0)
+        pb.flags = ((FLAG_TWO_PASS if two_pass else 0) | (FLAG_STREAM if stream else 0) | (FLAG_FUSED if fused else 0) |
+                    (FLAG_SELECT_ONE_WG if select_one_wg else 0))
         pb.ratio = float(ratio) if ratio is not None else 0.0
         pb.budget = int(budget) if budget is not None else 0
         pb.kv_head_stride, pb.kv_token_stride = int(kv_head_stride), int(kv_token_stride)
@@ -179,7 +181,7 @@ def _ptr(t):
 
 
 def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant=CAUSAL_WINDOW,
-              two_pass=False, stream=False, fused=False) -> Spec:
+              two_pass=False, stream=False, fused=False, select_one_wg=False) -> Spec:
     """Validate shapes of q_obs [B, H_q, L_obs, d] and K [H_kv, T, d] (any strides, last dim contiguous)."""
     if q_obs.dim() != 4 or K.dim() != 3:
         raise ValueError("q_obs must be [B, H_q, L_obs, d] and K [H_kv, T, d]")
@@ -201,7 +203,7 @@ def make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, vari
     return Spec(batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, obs_window=obs_window,
                 pool_kernel=pool_kernel, ratio=ratio, budget=budget, dtype=_dtype_code(K), cu_seqlens=cu,
                 kv_head_stride=K.stride(0), kv_token_stride=K.stride(1), variant=variant, two_pass=two_pass,
-                stream=stream, fused=fused)
+                stream=stream, fused=fused, select_one_wg=select_one_wg)
 
 
 def workspace(spec: Spec, device) -> torch.Tensor:
@@ -274,9 +276,11 @@ def scores(q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=Non
 
 
 def select(pooled, q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-           ws=None):
-    """snapkv_select over a given pooled vote: returns idx int32 [H_kv, sum_k]."""
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget)
+           ws=None, check_errors=True, select_one_wg=False):
+    """snapkv_select over a given pooled vote: returns idx int32 [H_kv, sum_k].  select_one_wg:
+    one workgroup per segment (SNAPKV_FLAG_SELECT_ONE_WG) instead of the split kernel.
+    check_errors: wait for the stream and raise SnapKVError if the workspace's error word is set."""
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, select_one_wg=select_one_wg)
     if pooled.dtype != torch.float32 or tuple(pooled.shape) != (spec.Hkv, spec.sum_P) or not pooled.is_contiguous():
         raise ValueError("pooled must be contiguous float32 [H_kv, sum_P]")
     idx = torch.empty((spec.Hkv, spec.sum_k), dtype=torch.int32, device=K.device)
@@ -285,6 +289,8 @@ def select(pooled, q_obs, K, cu_seqlens=None, *, obs_window=32, pool_kernel=7, r
     st = load().snapkv_select(ctypes.byref(spec.pb), _ptr(pooled), _ptr(idx), _ptr(ws),
                               ctypes.c_size_t(ws.numel()), _stream())
     _check(st, "snapkv_select")
+    if check_errors:
+        _raise_on_error_word(ws, "snapkv_select")
     return idx
 
 
@@ -305,7 +311,7 @@ def gather(K, V, idx, q_obs, cu_seqlens=None, *, obs_window=32, pool_kernel=7, r
 
 def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
              variant=CAUSAL_WINDOW, two_pass=False, want_pooled=False, ws=None, out=None, lse=None,
-             check_errors=True, stream=False, fused=False):
+             check_errors=True, stream=False, fused=False, select_one_wg=False):
     """snapkv_compress (snapkv_compress_lse when the rows' log-sum-exp `lse` [B, H_q, L_obs]
     is given): the whole path.
 
@@ -317,8 +323,10 @@ def compress(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, rati
     check_errors (default): wait for the stream and raise SnapKVError if the error word is set
     (a scoring barrier gave up, or the workspace was not clean).  check_errors=False returns at
     once; read res["error_word"] after the stream has reached the call.
+    select_one_wg: top-k with one workgroup per segment (SNAPKV_FLAG_SELECT_ONE_WG).
     """
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused)
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused,
+                     select_one_wg)
     if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
         raise ValueError("V must match K in shape, strides and dtype")
     dev = K.device
@@ -354,12 +362,14 @@ NOALLOC_SCRATCH_BYTES = 64 << 20  # SNAPKV_NOALLOC_SCRATCH_BYTES
 
 
 def compress_noalloc(q_obs, K, V, cu_seqlens=None, *, obs_window=32, pool_kernel=7, ratio=None, budget=None,
-                     variant=CAUSAL_WINDOW, two_pass=False, out=None, error_word=None, stream=False, fused=False):
+                     variant=CAUSAL_WINDOW, two_pass=False, out=None, error_word=None, stream=False, fused=False,
+                     select_one_wg=False):
     """snapkv_compress_noalloc: the whole path with the library's own device scratch as the
     workspace (the C call allocates nothing; the outputs are allocated here unless `out` gives
     them).  error_word: optional int32 device tensor of one element that receives the call's
     error bits.  Returns the same dict as compress() (without pooled unless out holds it)."""
-    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused)
+    spec = make_spec(q_obs, K, cu_seqlens, obs_window, pool_kernel, ratio, budget, variant, two_pass, stream, fused,
+                     select_one_wg)
     if V.shape != K.shape or V.stride() != K.stride() or V.dtype != K.dtype:
         raise ValueError("V must match K in shape, strides and dtype")
     dev = K.device

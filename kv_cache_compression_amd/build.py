@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = ["api.hip", "obs_score.hip", "obs_inst_bf16_d128.hip", "obs_inst_bf16_d64.hip", "obs_inst_f32_d128.hip",
            "obs_inst_f32_d64.hip", "obs_stream.hip", "obs_onepass.hip", "obs_onepass2.hip",
-           "select_gather.hip", "decode.hip"]
+           "select_gather.hip", "select_split.hip", "decode.hip"]
 LIB = os.path.join(PKG, "libsnapkv.so")
 
 HIPCC_FLAGS = [

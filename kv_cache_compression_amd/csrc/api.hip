@@ -61,6 +61,8 @@ struct Plan {
     // workspace layout (bytes)
     size_t off_err, off_cnt, off_partial, off_merged, off_planes, off_votes, off_pooled, off_idx;
     size_t off_long_state, off_ghist, off_cand, off_tilecnt;
+    size_t off_split_ctl, off_split_hist, off_split_rec;  // split select: counters, histograms, records
+    bool has_split;    // some segment is short enough for the split select
     size_t off_st_ticket, off_st_ctl, off_st_partial, off_st_final;
     size_t off_op_partial, off_op_final, ws_bytes;  // one-read kernel: tagged row stats, row shifts
 };
@@ -165,7 +167,7 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (p.dtype != SNAPKV_F32 && p.dtype != SNAPKV_BF16) return fail(SNAPKV_EINVAL, "dtype must be F32 or BF16");
     if (p.variant != SNAPKV_CAUSAL_WINDOW && p.variant != SNAPKV_PREFIX_ONLY)
         return fail(SNAPKV_EINVAL, "variant must be CAUSAL_WINDOW or PREFIX_ONLY");
-    if (p.flags & ~(SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED))
+    if (p.flags & ~(SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED | SNAPKV_FLAG_SELECT_ONE_WG))
         return fail(SNAPKV_EINVAL, "unknown flag bits");
     {
         const uint32_t path = p.flags & (SNAPKV_FLAG_TWO_PASS | SNAPKV_FLAG_STREAM | SNAPKV_FLAG_FUSED);
@@ -296,10 +298,21 @@ int make_plan(const snapkv_problem *pb, Plan *pl) {
     if (has_long) off = align_up(off + sizeof(LongState) * (size_t)p.max_group_segs);
     p.off_ghist = off;
     if (has_long) off = align_up(off + sizeof(uint32_t) * 4096 * (size_t)p.max_group_segs);
+    // split select (segments of up to select_lds_positions()): two counter lines and a histogram
+    // of 4096 + 64 words per segment (zero between calls, like the tile select's state), then
+    // per-chunk records after the candidates
+    p.has_split = false;
+    for (int r = 0; r < p.B; ++r) p.has_split = p.has_split || (p.P[r] > 0 && p.P[r] <= select_lds_positions());
+    p.off_split_ctl = off;
+    if (p.has_split) off = align_up(off + sizeof(uint32_t) * 2 * kSplitLine * (size_t)p.max_group_segs);
+    p.off_split_hist = off;
+    if (p.has_split) off = align_up(off + sizeof(uint32_t) * (4096 + 64) * (size_t)p.max_group_segs);
     p.off_cand = off;
-    if (has_long) off = align_up(off + sizeof(uint32_t) * (size_t)p.Hkv * (size_t)p.sum_P);
+    if (has_long || p.has_split) off = align_up(off + sizeof(uint32_t) * (size_t)p.Hkv * (size_t)p.sum_P);
     p.off_tilecnt = off;
     if (has_long) off = align_up(off + sizeof(uint32_t) * 4 * (size_t)p.max_tiles * (size_t)p.max_group_segs);
+    p.off_split_rec = off;
+    if (p.has_split) off = align_up(off + sizeof(uint32_t) * kSplitMaxChunks * (size_t)p.max_group_segs);
     // streaming scoring: ticket line, three control lines per segment, per-item row stats,
     // per-segment row shifts
     const size_t st_rows = (size_t)p.st_rows;
@@ -712,7 +725,50 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
         const bool any_k = p.cu_k[gr.rt.qi[gr.rt.n - 1] + 1] != p.cu_k[gr.rt.qi[0]];
         bool any_resident = false;  // a segment the resident kernel takes (the others return at once)
         for (int i = 0; i < gr.rt.n; ++i) any_resident = any_resident || gr.rt.L[i] - p.w <= select_lds_positions();
-        if (any_resident && (any_k || (fuse && pooled))) {
+        // Segments of up to select_lds_positions() go to the split kernel (workgroups of
+        // split_chunk() positions that wait for each other) when the group has one longer than
+        // 16 positions per thread of the single-workgroup kernel (its slowest runs: 20 against
+        // 10 us for 32K against 16K positions, where the split's two round trips pay) and the
+        // device holds the whole grid; else to one workgroup per segment.
+        SplitParams xp;
+        memset(&xp, 0, sizeof xp);
+        int64_t split_grid = 0;
+        for (int i = 0; i < gr.rt.n; ++i) {
+            xp.wg0[i] = (int32_t)split_grid;
+            const int64_t P = gr.rt.L[i] - p.w;
+            if (P > 0 && P <= select_lds_positions()) split_grid += (int64_t)p.Hkv * ((P + split_chunk() - 1) / split_chunk());
+        }
+        xp.wg0[gr.rt.n] = (int32_t)split_grid;
+        bool use_split = false;
+        if (any_resident && (any_k || (fuse && pooled)) && p.has_split && split_grid > 0 &&
+            gr.max_P > 16 * select_threads() && !(p.flags & SNAPKV_FLAG_SELECT_ONE_WG) &&
+            (!fuse || p.K_pool / 2 <= split_max_half())) {
+            DevInfo di;
+            int st = device_info(&di);
+            if (st) return st;
+            use_split = split_grid <= (int64_t)occupancy(split_kernel(), split_threads()) * di.cus;
+        }
+        if (use_split) {
+            xp.votes = fuse ? votes : nullptr;
+            xp.pooled = pooled;
+            xp.pooled_out = fuse ? pooled : nullptr;
+            xp.idx = idx;
+            xp.ctl = (uint32_t *)(ws + p.off_split_ctl);
+            xp.ghist = (uint32_t *)(ws + p.off_split_hist);
+            xp.cand = (uint32_t *)(ws + p.off_cand);
+            xp.rec = (uint32_t *)(ws + p.off_split_rec);
+            xp.err = (uint32_t *)(ws + p.off_err);
+            xp.sum_P = p.sum_P;
+            xp.sum_k = p.sum_k;
+            xp.w = p.w;
+            xp.Hkv = p.Hkv;
+            xp.half = p.K_pool / 2;
+            xp.spin_limit = kSpinLimit;
+            xp.rt = gr.rt;
+            int st = launch(SNAPKV_K_SELECT_SPLIT, split_kernel(), dim3((unsigned)split_grid), dim3(split_threads()), &xp,
+                            stream);
+            if (st) return st;
+        } else if (any_resident && (any_k || (fuse && pooled))) {
             SelectParams sp;
             memset(&sp, 0, sizeof sp);
             sp.votes = fuse ? votes : nullptr;
@@ -844,7 +900,7 @@ static int control_ranges(const Plan &p, CtlRange *r) {
         if (b > a) r[n++] = CtlRange{a, b - a};
     };
     add(p.off_cnt, p.off_partial);         // arrival lines
-    add(p.off_long_state, p.off_cand);     // tile select: state, histograms
+    add(p.off_long_state, p.off_cand);     // tile and split selects: state, counters, histograms
     add(p.off_st_ticket, p.off_st_partial);  // ticket line, control lines
     add(p.off_op_partial, p.ws_bytes);     // tagged stats and shifts
     return n;
@@ -1243,6 +1299,7 @@ const char *snapkv_kernel_name(int id) {
         case SNAPKV_K_HIT_CLEAR: return "hit_rate_clear";
         case SNAPKV_K_SCRATCH_CLEAR: return "scratch_clear";
         case SNAPKV_K_WS_CLEAR: return "ws_clear";
+        case SNAPKV_K_SELECT_SPLIT: return "topk_select_split";
         case SNAPKV_K_OBS_STREAM: return "obs_score_stream";
         case SNAPKV_K_OBS_ONEPASS: return "obs_score_onepass";
         case SNAPKV_K_OBS_ONEPASS2: return "obs_score_onepass2";

@@ -191,6 +191,32 @@ const void *long_kernel();
 int select_tile_positions();
 int long_threads();             // workgroup size of long_kernel
 
+// Top-k with a segment of up to 32768 positions split over workgroups of split_chunk()
+// positions that wait for each other (every workgroup of the launch must be resident at once).
+constexpr int kSplitLine = 64;       // uint32 words per counter line
+constexpr int kSplitMaxChunks = 4;   // chunks of the longest segment it takes
+struct SplitParams {
+    const float *votes;         // raw votes to pool, or null (pooled given)
+    const float *pooled;        // pooled votes to select from when votes is null
+    float *pooled_out;          // pooled votes written here when pooling here, or null
+    int32_t *idx;
+    uint32_t *ctl;              // [segments][2 lines]: the two meetings' counters (zero between calls)
+    uint32_t *ghist;            // [segments][4096 + 64]: histogram of bits 30..19, its block sums (zero between calls)
+    uint32_t *cand;             // [H_kv][sum_P]: each chunk's candidates in its own columns
+    uint32_t *rec;              // [segments][kSplitMaxChunks]: (count above the bin) | (count in it) << 16
+    uint32_t *err;              // error word (bit 0: a wait gave up)
+    int64_t sum_P, sum_k;
+    int32_t w, Hkv, half;       // half = K_pool / 2 (<= split_max_half())
+    uint32_t spin_limit;
+    int32_t wg0[kMaxReq + 1];   // first workgroup of each request's segments (no workgroups when
+                                // P <= 0 or P > 32768)
+    ReqTable rt;
+};
+const void *split_kernel();
+int split_threads();
+int split_chunk();
+int split_max_half();
+
 struct HitParams {
     const float *a_cur;         // [H_kv][sum_P]
     const int32_t *idx;         // [H_kv][sum_k], ascending per segment

@@ -303,10 +303,14 @@ def test_onepass2_segment_limit(extra):
 SELECT_P = [1, 2, 3, 4096, 4097, 8192, 8193, 16384, 16385, 32768, 32769, 49152, 57345, 65535, 70001]
 
 
+@pytest.mark.parametrize("one_wg", [False, True], ids=["split", "one_wg"])
 @pytest.mark.parametrize("levels", [0, 3, 50])
-def test_select_exact_on_crafted_votes(levels):
+def test_select_exact_on_crafted_votes(levels, one_wg):
     """snapkv_select on given non-negative values equals the oracle's select exactly: heavy
-    ties (few distinct levels), exact zeros and negative zeros (which order as +0)."""
+    ties (few distinct levels), exact zeros and negative zeros (which order as +0).  Both
+    kernels for segments of up to 32768 positions: split over 8192-position workgroups (with
+    three levels a 32768-position segment has about 11000 candidates in the pivot bin, more than
+    the 8192 a workgroup holds in LDS) and one workgroup per segment."""
     snap = _snap()
     w = 4
     lengths = [p + w for p in SELECT_P]
@@ -324,9 +328,12 @@ def test_select_exact_on_crafted_votes(levels):
     vals[:, rng.integers(0, sum_P, 100)] = np.float32(0.0)
     pooled = torch.from_numpy(vals).cuda()
     for kw in (dict(ratio=0.37), dict(budget=1), dict(budget=4097), dict(ratio=1.0)):
-        _say("select levels=%d %s" % (levels, kw))
+        _say("select levels=%d one_wg=%s %s" % (levels, one_wg, kw))
         spec = snap.make_spec(q, K, cu, w, 7, kw.get("ratio"), kw.get("budget"))
-        idx = snap.select(pooled, q, K, cu, obs_window=w, pool_kernel=7, **kw)
+        ids = _launched_kernels(lambda: snap.select(pooled, q, K, cu, obs_window=w, pool_kernel=7,
+                                                    select_one_wg=one_wg, **kw))
+        assert (6 if one_wg else 19) in ids and (19 if one_wg else 6) not in ids, "launched %s" % ids
+        idx = snap.select(pooled, q, K, cu, obs_window=w, pool_kernel=7, select_one_wg=one_wg, **kw)
         torch.cuda.synchronize()
         idx = idx.cpu().numpy()
         pfx = np.concatenate([[0], np.cumsum(SELECT_P)])
@@ -337,6 +344,43 @@ def test_select_exact_on_crafted_votes(levels):
                 got = idx[g, int(spec.cu_k[r]):int(spec.cu_k[r + 1])]
                 np.testing.assert_array_equal(got.astype(np.int64), oracle.select(seg, k).astype(np.int64),
                                               err_msg="P=%d k=%d g=%d %s" % (P, k, g, kw))
+
+
+# The split select (taken when a launch group has a segment of more than 16384 positions)
+# against one workgroup per segment through the whole call (pooling fused into the select):
+# bit-identical pooled votes and indices.  Segments of one chunk beside a longer one, a ragged
+# last chunk, exactly 4 chunks, a batch mixing them with a segment for the tile kernel, grouped
+# heads, a wide pool window (half-width 16, the widest either kernel pools), budget mode, and
+# requests with an empty prefix, with k = 0 (8 positions) and with k = P (1 position).
+SPLIT_CASES = [
+    # name, lengths, Hq, Hkv, d, w, K_pool, ratio, budget
+    ("split_one_chunk", [20000, 2000, 600, 32], 4, 4, 64, 32, 7, 0.05, None),
+    ("split_ragged", [9000, 20001], 4, 2, 64, 16, 7, 0.05, None),
+    ("split_4_chunks", [32768 + 32], 2, 2, 64, 32, 7, 0.1, None),
+    ("split_with_tiles", [40000, 5000, 32768 + 32, 40], 4, 2, 64, 32, 13, 0.05, None),
+    ("split_pool33", [20000, 3000], 4, 4, 64, 16, 33, 0.05, None),
+    ("split_budget", [7000, 25000, 33], 8, 2, 64, 32, 7, None, 1000),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_select_matches_one_workgroup(case):
+    name, lengths, Hq, Hkv, d, w, kp, ratio, budget = case
+    wl = synth.custom(lengths, Hq, Hkv, d, obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, n_plant=8,
+                      name=name)
+    x = synth.make_inputs(wl, 0, threads=16)
+    snap = _snap()
+    q, K, V = to_torch(x["q_obs"]), to_torch(x["K"]), to_torch(x["V"])
+    kw = dict(obs_window=w, pool_kernel=kp, ratio=ratio, budget=budget, want_pooled=True)
+    _say("split select %s" % name)
+    ids = _launched_kernels(lambda: snap.compress(q, K, V, x["cu_seqlens"], **kw))
+    assert 19 in ids and 6 not in ids, "expected the split select, launched %s" % ids
+    a = snap.compress(q, K, V, x["cu_seqlens"], **kw)
+    b = snap.compress(q, K, V, x["cu_seqlens"], select_one_wg=True, **kw)
+    torch.cuda.synchronize()
+    for key in ("pooled", "idx", "K_out", "V_out"):
+        assert torch.equal(a[key], b[key]), "%s: %s differs between the two select kernels" % (name, key)
+    run_and_check(wl, inputs=x)
 
 
 LSE_CASES = [
