@@ -740,13 +740,22 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
         }
         xp.wg0[gr.rt.n] = (int32_t)split_grid;
         bool use_split = false;
+        int split_thr = 0;
         if (any_resident && (any_k || (fuse && pooled)) && p.has_split && split_grid > 0 &&
             gr.max_P > 16 * select_threads() && !(p.flags & SNAPKV_FLAG_SELECT_ONE_WG) &&
             (!fuse || p.K_pool / 2 <= split_max_half())) {
             DevInfo di;
             int st = device_info(&di);
             if (st) return st;
-            use_split = split_grid <= (int64_t)occupancy(split_kernel(), split_threads()) * di.cus;
+            // 1024 threads per workgroup where the grid is resident at one per CU, else 512
+            // threads (more of them stay resident)
+            for (int t : {1024, 512}) {
+                if (split_grid <= (int64_t)occupancy(split_kernel(t), t) * di.cus) {
+                    split_thr = t;
+                    break;
+                }
+            }
+            use_split = split_thr > 0;
         }
         if (use_split) {
             xp.votes = fuse ? votes : nullptr;
@@ -765,7 +774,7 @@ int run_select(const Plan &p, const float *votes, float *pooled, int32_t *idx, c
             xp.half = p.K_pool / 2;
             xp.spin_limit = kSpinLimit;
             xp.rt = gr.rt;
-            int st = launch(SNAPKV_K_SELECT_SPLIT, split_kernel(), dim3((unsigned)split_grid), dim3(split_threads()), &xp,
+            int st = launch(SNAPKV_K_SELECT_SPLIT, split_kernel(split_thr), dim3((unsigned)split_grid), dim3(split_thr), &xp,
                             stream);
             if (st) return st;
         } else if (any_resident && (any_k || (fuse && pooled))) {

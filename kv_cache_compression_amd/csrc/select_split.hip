@@ -35,10 +35,7 @@ namespace snapkv {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kRun = 8;                     // positions per thread
-constexpr int kChunk = kThreads * kRun;     // positions per workgroup
+constexpr int kChunk = 8192;                // positions per workgroup
 constexpr int kHalo = 16;                   // widest pool half-width pooled here
 constexpr int kStage = kChunk + 2 * kHalo;  // staged votes: the chunk and its halo
 constexpr int kBins = 4096;                 // first digit: bits 30..19
@@ -47,8 +44,8 @@ constexpr int kRefBins = 2048;              // refinement digits: bits 18..8, th
 constexpr int kMaxChunks = kSplitMaxChunks;
 constexpr int kCandLds = kChunk;            // candidates held in LDS; more are re-read per pass
 static_assert(kStage >= kCandLds && kBins >= kRefBins, "buffer reuse");
-static_assert(kBins == 4 * kThreads, "each thread adds 4 bins of one block");
 
+template <int kWaves>
 struct SplitShared {
     uint32_t stage[kStage];          // the votes and their halo; then the candidates
     uint32_t hist[kBins];            // the chunk's first histogram; then the refinement histograms
@@ -88,6 +85,7 @@ __device__ inline void meet(uint32_t *ctr, uint32_t n, const SplitParams &p) {
 
 // Exclusive prefix sum of x over the workgroup; *total gets the sum.  Ends with the barrier
 // after which wtot is read, so two calls in a row need a barrier between them.
+template <int kWaves>
 __device__ inline uint32_t excl_scan(uint32_t x, uint32_t *total, uint32_t *wtot) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_incl_scan(x);
@@ -137,8 +135,15 @@ __device__ inline void find_bin_lds(const uint32_t *hist, uint32_t need, uint32_
 
 }  // namespace
 
+// kThreads threads of kChunk / kThreads positions each (1024 x 8, or 512 x 16 where the device
+// keeps more 512-thread workgroups resident).
+template <int kThreads>
 __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams p) {
-    __shared__ __attribute__((aligned(16))) SplitShared s;
+    constexpr int kWaves = kThreads / 64;
+    constexpr int kRun = kChunk / kThreads;  // positions per thread
+    constexpr int kBpt = kBins / kThreads;   // first-histogram bins each thread adds (one block's)
+    static_assert(kRun * kThreads == kChunk && kBpt * kThreads == kBins && kBpt % 4 == 0, "shape");
+    __shared__ __attribute__((aligned(16))) SplitShared<kWaves> s;
     const int tid = threadIdx.x, lane = tid & 63;
     // workgroup -> (request, KV head, chunk)
     const int b = (int)blockIdx.x;
@@ -209,19 +214,21 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
     });
     __syncthreads();
     {
-        // thread t adds bins 4t .. 4t + 3, which all lie in block t / 16
+        // thread t adds bins kBpt t .. kBpt t + kBpt - 1, which all lie in block t / (64 / kBpt)
+        constexpr int kTpb = kBlockBins / kBpt;  // threads per block of bins
         uint32_t bsum = 0;
-        const u32x4_t h4 = *(const u32x4_t *)&s.hist[4 * tid];
-        static_for<4>([&](auto e) {
-            const uint32_t c = h4[e()];
-            if (c) __hip_atomic_fetch_add(&gh[4 * tid + e()], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            bsum += c;
+        static_for<kBpt / 4>([&](auto q) {
+            const u32x4_t h4 = *(const u32x4_t *)&s.hist[kBpt * tid + 4 * q()];
+            static_for<4>([&](auto e) {
+                const uint32_t c = h4[e()];
+                if (c) __hip_atomic_fetch_add(&gh[kBpt * tid + 4 * q() + e()], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bsum += c;
+            });
         });
-        bsum += __shfl_xor(bsum, 1);
-        bsum += __shfl_xor(bsum, 2);
-        bsum += __shfl_xor(bsum, 4);
-        bsum += __shfl_xor(bsum, 8);
-        if ((tid & 15) == 0 && bsum) __hip_atomic_fetch_add(&gblk[tid >> 4], bsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int o = 1; o < kTpb; o <<= 1) bsum += __shfl_xor(bsum, o);
+        if ((tid & (kTpb - 1)) == 0 && bsum)
+            __hip_atomic_fetch_add(&gblk[tid / kTpb], bsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     meet(&ctl[0], (uint32_t)C, p);
     if (tid < 64) {
@@ -255,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
         c_eq += i() < nvalid && m == pv.prefix ? 1u : 0u;
     });
     uint32_t tot;
-    const uint32_t ex = excl_scan(c_gt | (c_eq << 16), &tot, s.wtot);  // counts fit 16 bits (<= 8192)
+    const uint32_t ex = excl_scan<kWaves>(c_gt | (c_eq << 16), &tot, s.wtot);  // counts fit 16 bits (<= 8192)
     uint32_t *const cand = p.cand + base + c0;  // this chunk's columns
     if (!whole) {
         uint32_t o = ex >> 16;
@@ -356,8 +363,8 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
             e1 += m == pv.prefix ? 1u : 0u;
         });
         uint32_t gsum, esum;
-        (void)excl_scan(g1, &gsum, s.wtot);
-        (void)excl_scan(e1, &esum, s.wtot2);
+        (void)excl_scan<kWaves>(g1, &gsum, s.wtot);
+        (void)excl_scan<kWaves>(e1, &esum, s.wtot2);
         gt_base = above_before + gsum;
         eq_base = esum;
     }
@@ -370,7 +377,7 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
     });
     __syncthreads();  // wtot is reused
     uint32_t total;
-    const uint32_t ex2 = excl_scan(packed, &total, s.wtot);
+    const uint32_t ex2 = excl_scan<kWaves>(packed, &total, s.wtot);
     uint32_t gt_before = gt_base + (ex2 & 0xFFFFu), eq_before = eq_base + (ex2 >> 16);
     static_for<kRun>([&](auto i) {
         const uint32_t m = u[i()] & pv.mask;
@@ -386,8 +393,9 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
     }
 }
 
-const void *split_kernel() { return (const void *)&topk_split_kernel; }
-int split_threads() { return kThreads; }
+const void *split_kernel(int threads) {
+    return threads == 512 ? (const void *)&topk_split_kernel<512> : (const void *)&topk_split_kernel<1024>;
+}
 int split_chunk() { return kChunk; }
 int split_max_half() { return kHalo; }
 

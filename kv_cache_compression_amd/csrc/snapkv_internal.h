@@ -212,8 +212,7 @@ struct SplitParams {
                                 // P <= 0 or P > 32768)
     ReqTable rt;
 };
-const void *split_kernel();
-int split_threads();
+const void *split_kernel(int threads);  // 1024 (8 positions per thread) or 512 (16)
 int split_chunk();
 int split_max_half();
 

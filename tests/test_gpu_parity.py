@@ -351,7 +351,8 @@ def test_select_exact_on_crafted_votes(levels, one_wg):
 # bit-identical pooled votes and indices.  Segments of one chunk beside a longer one, a ragged
 # last chunk, exactly 4 chunks, a batch mixing them with a segment for the tile kernel, grouped
 # heads, a wide pool window (half-width 16, the widest either kernel pools), budget mode, and
-# requests with an empty prefix, with k = 0 (8 positions) and with k = P (1 position).
+# requests with an empty prefix, with k = 0 (8 positions) and with k = P (1 position), and a
+# grid large enough for the 512-thread workgroups.
 SPLIT_CASES = [
     # name, lengths, Hq, Hkv, d, w, K_pool, ratio, budget
     ("split_one_chunk", [20000, 2000, 600, 32], 4, 4, 64, 32, 7, 0.05, None),
@@ -360,6 +361,8 @@ SPLIT_CASES = [
     ("split_with_tiles", [40000, 5000, 32768 + 32, 40], 4, 2, 64, 32, 13, 0.05, None),
     ("split_pool33", [20000, 3000], 4, 4, 64, 16, 33, 0.05, None),
     ("split_budget", [7000, 25000, 33], 8, 2, 64, 32, 7, None, 1000),
+    # 320 workgroups: past one 1024-thread workgroup per CU, so the 512-thread kernel runs
+    ("split_512_threads", [20000] * 12 + [3000] * 4, 8, 8, 64, 32, 7, 0.05, None),
 ]
 
 
