@@ -161,6 +161,7 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
     const int j0 = c0 + kRun * tid;
     const int nvalid = P - j0 < 0 ? 0 : (P - j0 > kRun ? kRun : P - j0);
 
+    for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;  // published by the staging barrier
     // ---- this chunk's pooled values: u[i] is position j0 + i ----
     uint32_t u[kRun];
     if (p.votes) {
@@ -207,11 +208,24 @@ __global__ void __launch_bounds__(kThreads) topk_split_kernel(const SplitParams 
     uint32_t *const gblk = gh + kBins;
 
     // ---- meeting 1: the segment's histogram of bits 30..19 ----
-    for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
-    __syncthreads();
-    static_for<kRun>([&](auto i) {
-        if (i() < nvalid) atomicAdd(&s.hist[u[i()] >> 19], 1u);
-    });
+    // (the histogram was zeroed while the votes were staged; a run of equal digits in a thread's
+    // positions -- max pooling makes plateaus -- is added once)
+    if (!p.votes) __syncthreads();  // no staging barrier: the zeroing is published here
+    {
+        uint32_t cur = u[0] >> 19, cnt = 0;
+        static_for<kRun>([&](auto i) {
+            if (i() < nvalid) {
+                const uint32_t d = u[i()] >> 19;
+                if (d != cur) {
+                    if (cnt) atomicAdd(&s.hist[cur], cnt);
+                    cur = d;
+                    cnt = 0;
+                }
+                ++cnt;
+            }
+        });
+        if (cnt) atomicAdd(&s.hist[cur], cnt);
+    }
     __syncthreads();
     {
         // thread t adds bins kBpt t .. kBpt t + kBpt - 1, which all lie in block t / (64 / kBpt)
