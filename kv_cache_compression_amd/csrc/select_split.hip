@@ -1,5 +1,5 @@
 // select_split.hip -- pooling and top-k selection with each (request, KV head) segment split over
-// workgroups of 2048 positions that meet twice, gfx950.
+// workgroups of 8192 positions that meet twice, gfx950.
 //
 // What is computed (page "論文解説: SnapKV — アテンションパターン観測によるKVキャッシュ圧縮"):
 //   * クラスタリングによる文脈保持: the votes are max pooled (width K_pool, stride 1, padding
@@ -10,12 +10,15 @@
 // values.
 //
 // How it maps to CDNA4.  A segment of P <= 32768 positions takes ceil(P / 8192) workgroups of
-// 1024 threads; each thread holds a run of 8 positions in registers, pooled from the votes staged
-// in LDS with their halo.  The host launches this kernel only when the device holds its whole
-// grid at once, so the workgroups of a segment may wait for each other.  They meet twice:
+// 1024 threads (or 512 where more workgroups must be resident); each thread holds a run of 8 (16)
+// consecutive positions in registers, pooled from the votes staged in LDS with their halo.  The
+// host launches this kernel only when the device holds its whole grid at once, so the
+// workgroups of a segment may wait for each other.  They meet twice:
 //   1. Each adds the 4096-bin histogram of bits 30..19 of its values (and the sums of its 64
-//      blocks of 64 bins) to the segment's histogram in memory, then arrives.  Once every chunk
-//      has arrived, each reads the block sums and one block: the bin b of the k-th value.
+//      blocks of 64 bins) to the segment's histogram in memory, then arrives; a run of equal
+//      bins in a thread's positions (max pooling makes plateaus) is added to the LDS histogram
+//      once.  Once every chunk has arrived, each reads the block sums and one block: the bin b
+//      of the k-th value.
 //   2. Each writes its values in bin b to its own columns of a candidate array and one record
 //      (its count above b, its count in b), then arrives.  Once every chunk has arrived, each
 //      reads the records and, unless bin b is kept whole, every candidate: it refines the k-th
